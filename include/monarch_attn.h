@@ -1,0 +1,157 @@
+/*
+ * monarch_attn.h -- C ABI of the gfx950 (MI355X) Monarch video-attention library.
+ *
+ * The operation (MonarchRT pages: author abstract; gist.science explainer,
+ * section 2 "Methodology", parts A "Block Alignment" and B "Tiled Monarch
+ * Parameterization"): attention over the N = T*H*W tokens of a video is
+ * replaced by a Monarch matrix, the product of two block-diagonal factors with
+ * a stride permutation between them, with blocks aligned to the video grid.
+ * The factor formulas are not printed on the pages; this library fixes them:
+ *
+ *   tokens in (t, h, w) row-major order, n = (t*H + h)*W + w;
+ *   block size b (alignment), tile tau (whole blocks, tau | N), m_tau = tau/b;
+ *   token n = u*tau + i*b + j  (tile u, block i inside the tile, position j);
+ *   stage 1:  Y[u,i,j] = sum_j' softmax_j'(s <Q[u,i,j], K[u,i,j']>) V[u,i,j']
+ *   stage 2:  O[u,i,j] = sum_i' softmax_i'(s <Q[u,i,j], K[u,i',j]>) Y[u,i',j]
+ *   s = 1/sqrt(head_dim) unless a scale is given.
+ *
+ * Non-causal (explainer section 2.C). Every row of every block and group has
+ * at least one key, so no row is empty.
+ *
+ * Layout: Q, K, V, O are dense row-major [batch, heads, N, head_dim] arrays of
+ * one element type (bf16 or fp32), in device memory, 16-byte aligned. The
+ * stage-1 intermediate Y has the same shape and lives in a caller-provided
+ * device workspace.
+ *
+ * Ownership: the caller owns every device buffer. A plan holds host metadata
+ * only; it never allocates device memory. No entry point allocates device
+ * memory, synchronises the host, or keeps global mutable state, so forwards on
+ * different streams with different workspaces may run concurrently with one
+ * plan.
+ *
+ * Errors: every argument, plan and pointer check returns its status before any
+ * HIP call, so these paths are testable on a machine without a GPU. A failed
+ * kernel launch returns MONARCH_ERR_HIP. No C++ exception crosses this ABI.
+ * Inf or NaN inputs are not checked; they propagate.
+ */
+#ifndef MONARCH_ATTN_H
+#define MONARCH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MONARCH_ABI_VERSION 1
+
+typedef enum monarch_status {
+  MONARCH_OK = 0,
+  MONARCH_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, unknown enum, overflow */
+  MONARCH_ERR_UNSUPPORTED = 2,  /* head_dim or dtype this build does not implement */
+  MONARCH_ERR_UNALIGNED = 3,    /* b does not divide N, tile not whole blocks, split cuts a grid axis,
+                                   or a device pointer not 16-byte aligned */
+  MONARCH_ERR_WORKSPACE = 4,    /* workspace null or smaller than monarch_attn_workspace_size() */
+  MONARCH_ERR_ALIAS = 5,        /* output overlaps an input or the workspace */
+  MONARCH_ERR_HIP = 6           /* a HIP launch failed */
+} monarch_status;
+
+typedef enum monarch_dtype {
+  MONARCH_BF16 = 0,  /* bfloat16 storage, fp32 accumulation and softmax */
+  MONARCH_FP32 = 1   /* fp32 storage and arithmetic (no reduced-precision products) */
+} monarch_dtype;
+
+/* Block alignment (explainer section 2.A): each video axis lies inside exactly one of the two
+ * Monarch block dimensions. */
+typedef enum monarch_align {
+  MONARCH_ALIGN_FRAME = 0,   /* b = H*W: a block is one frame, a group is one (h,w) across frames */
+  MONARCH_ALIGN_ROW = 1,     /* b = W: a block is one spatial row, a group is one w across (t,h) */
+  MONARCH_ALIGN_DENSE = 2,   /* b = N, m = 1: ordinary softmax attention (the dense comparison) */
+  MONARCH_ALIGN_TOKEN = 3,   /* b = 1, m = N: ordinary softmax attention through stage 2 alone */
+  MONARCH_ALIGN_CUSTOM = 4   /* b = custom_b; must divide N; needs MONARCH_FLAG_ALLOW_UNALIGNED
+                                unless b is one of W, H*W, 1, N */
+} monarch_align;
+
+#define MONARCH_FLAG_Y_FP32 (1u << 0)          /* keep Y in fp32 for bf16 inputs (default: bf16) */
+#define MONARCH_FLAG_ALLOW_UNALIGNED (1u << 1) /* accept a custom b that cuts a grid axis */
+#define MONARCH_FLAG_GENERIC (1u << 2)         /* force the plain VALU kernels (diagnostics) */
+
+typedef struct monarch_plan monarch_plan;
+
+typedef struct monarch_plan_info {
+  int64_t batch, heads, head_dim;
+  int64_t T, H, W, N;
+  int64_t b;          /* block size */
+  int64_t tau;        /* tile size in tokens (N when untiled) */
+  int64_t m_tau;      /* blocks per tile = stage-2 group size */
+  int64_t tiles;      /* U = N / tau */
+  int32_t dtype;      /* monarch_dtype of Q, K, V, O */
+  int32_t y_dtype;    /* monarch_dtype of the workspace Y */
+  float scale;        /* softmax scale s */
+  uint32_t flags;
+  int64_t workspace_bytes;
+  int64_t flops_stage1;  /* 4*batch*heads*N*b*head_dim (0 when stage 1 is skipped, b = 1) */
+  int64_t flops_stage2;  /* 4*batch*heads*N*m_tau*head_dim (0 when stage 2 is skipped, m_tau = 1) */
+  int32_t stage1_kernel; /* variant id, see monarch_attn_kernel_name() */
+  int32_t stage2_kernel;
+} monarch_plan_info;
+
+/* Validate a problem and build a plan (host only, no HIP call).
+ *   out          receives the plan on MONARCH_OK (else *out is set to NULL).
+ *   batch, heads >= 1; head_dim in {64, 128}; T, H, W >= 1, N = T*H*W < 2^31.
+ *   align        monarch_align; custom_b is read only for MONARCH_ALIGN_CUSTOM.
+ *   tile_tokens  0 = untiled (tau = N); else tau, a multiple of b dividing N
+ *                (explainer section 2.B: each large block cut into sub-blocks).
+ *   dtype        monarch_dtype; scale 0 = 1/sqrt(head_dim); flags MONARCH_FLAG_*. */
+monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t heads, int32_t head_dim,
+                                 int32_t T, int32_t H, int32_t W, int32_t align, int64_t custom_b,
+                                 int64_t tile_tokens, int32_t dtype, float scale, uint32_t flags);
+
+/* Free a plan (NULL is ignored). */
+void monarch_attn_destroy(monarch_plan* plan);
+
+/* Bytes of device workspace monarch_attn_forward needs (0 when b = 1 or m_tau = 1). */
+size_t monarch_attn_workspace_size(const monarch_plan* plan);
+
+/* Copy the plan's derived sizes into *info. */
+monarch_status monarch_attn_plan_info(const monarch_plan* plan, monarch_plan_info* info);
+
+/* Full forward O = stage2(Q, K, stage1(Q, K, V)) on `stream` (a hipStream_t; NULL = default
+ * stream). Asynchronous: returns after enqueueing. q, k, v, o: device pointers to
+ * [batch, heads, N, head_dim] arrays of the plan's dtype. workspace: device memory of at least
+ * monarch_attn_workspace_size() bytes (may be NULL when that is 0); its contents on entry are
+ * ignored and on return are Y. o must not overlap q, k, v or the workspace. When m_tau = 1 the
+ * second factor is the identity and stage 1 writes O directly; when b = 1 the first factor is
+ * the identity and stage 2 reads V. */
+monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, const void* k,
+                                    const void* v, void* o, void* workspace,
+                                    size_t workspace_bytes, void* stream);
+
+/* Stage 1 alone (the right factor, contiguous blocks): writes Y, an array of the plan's y_dtype
+ * and shape [batch, heads, N, head_dim], of y_bytes >= workspace size. When m_tau = 1 Y is the
+ * final output and has the input dtype. Returns MONARCH_ERR_INVALID_ARG when b = 1 (stage 1 is
+ * the identity). */
+monarch_status monarch_attn_stage1(const monarch_plan* plan, const void* q, const void* k,
+                                   const void* v, void* y, size_t y_bytes, void* stream);
+
+/* Stage 2 alone (the left factor, stride-b groups inside each tile): reads Y (plan's y_dtype;
+ * the input dtype when b = 1, where Y is V) and writes O. Returns MONARCH_ERR_INVALID_ARG when
+ * m_tau = 1 (stage 2 is the identity). */
+monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, const void* k,
+                                   const void* y, void* o, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* monarch_status_string(monarch_status status);
+
+/* Static name of a kernel variant id from monarch_plan_info (never NULL). */
+const char* monarch_attn_kernel_name(int32_t kernel_id);
+
+/* MONARCH_ABI_VERSION of the loaded library. */
+int32_t monarch_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MONARCH_ATTN_H */

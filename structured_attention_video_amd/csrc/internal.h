@@ -1,0 +1,57 @@
+// Internal launch interface between the C-ABI layer and the kernels.
+//
+// Both Monarch stages are instances of one primitive, "grouped attention":
+// a head is split into `problems` independent softmax-attention problems of L
+// rows each. Problem p owns the tokens
+//     base(p) + r * row_stride,  r = 0..L-1,
+//     base(p) = (p / inner) * outer + (p % inner),
+// and every row attends to every row of its own problem (keys = the same
+// tokens). Stage 1 (contiguous blocks): inner = 1, outer = b, row_stride = 1,
+// L = b. Stage 2 (stride-b groups inside tile u): inner = b, outer = tau,
+// row_stride = b, L = m_tau. Dense attention is stage 1 with b = N.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace monarch {
+
+enum ElemType : int32_t { kBF16 = 0, kF32 = 1 };
+
+struct GroupedArgs {
+  const void* q;
+  const void* k;
+  const void* v;      // values (V in stage 1, Y in stage 2)
+  void* o;            // output (Y in stage 1, O in stage 2)
+  int64_t head_elems; // elements between consecutive heads (N * D)
+  int32_t heads;      // batch * heads
+  int32_t problems;   // problems per head
+  int32_t inner;
+  int64_t outer;
+  int64_t row_stride; // in tokens
+  int32_t L;          // rows per problem
+  int32_t D;          // head dim
+  float scale_log2;   // softmax scale * log2(e)
+  ElemType qk_type;
+  ElemType v_type;
+  ElemType o_type;
+};
+
+// Kernel variant ids (reported through the plan info).
+enum KernelId : int32_t {
+  kKernelNone = 0,
+  kKernelGeneric = 1,   // plain VALU, fp32 arithmetic, any L
+  kKernelFlash = 2,     // bf16 MFMA, LDS-staged K/V tiles, online softmax, large L
+  kKernelSmall = 3,     // bf16 MFMA, one wavefront per problem, L <= 32
+  kKernelTiny = 4,      // VALU, one problem per thread group, L <= 8
+};
+
+const char* kernel_name(int32_t id);
+
+// Each launcher returns hipSuccess or the launch error.
+hipError_t launch_generic(const GroupedArgs& a, hipStream_t stream);
+bool flash_supported(const GroupedArgs& a);
+hipError_t launch_flash(const GroupedArgs& a, hipStream_t stream);
+bool small_supported(const GroupedArgs& a);
+hipError_t launch_small(const GroupedArgs& a, hipStream_t stream);
+
+}  // namespace monarch

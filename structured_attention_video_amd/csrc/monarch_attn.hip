@@ -1,0 +1,269 @@
+// C-ABI layer: plan validation, workspace sizing, pointer checks and kernel
+// dispatch for the two Monarch stages. Everything before a launch is plain
+// host arithmetic, so every error path runs without a GPU.
+#include "../../include/monarch_attn.h"
+
+#include <math.h>
+#include <new>
+
+#include "internal.h"
+
+using namespace monarch;
+
+struct monarch_plan {
+  monarch_plan_info info;
+};
+
+namespace {
+
+constexpr uint32_t kKnownFlags =
+    MONARCH_FLAG_Y_FP32 | MONARCH_FLAG_ALLOW_UNALIGNED | MONARCH_FLAG_GENERIC;
+
+size_t elem_bytes(int32_t dt) { return dt == MONARCH_FP32 ? 4 : 2; }
+
+int64_t tensor_bytes(const monarch_plan_info& p, int32_t dt) {
+  return p.batch * p.heads * p.N * p.head_dim * static_cast<int64_t>(elem_bytes(dt));
+}
+
+ElemType as_elem(int32_t dt) { return dt == MONARCH_FP32 ? kF32 : kBF16; }
+
+// Grouped-attention description of stage 1 (contiguous blocks of b tokens).
+GroupedArgs stage1_args(const monarch_plan_info& p, const void* q, const void* k, const void* v,
+                        void* out, int32_t out_dtype) {
+  GroupedArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = out;
+  a.head_elems = p.N * p.head_dim;
+  a.heads = static_cast<int32_t>(p.batch * p.heads);
+  a.problems = static_cast<int32_t>(p.N / p.b);
+  a.inner = 1;
+  a.outer = p.b;
+  a.row_stride = 1;
+  a.L = static_cast<int32_t>(p.b);
+  a.D = static_cast<int32_t>(p.head_dim);
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.qk_type = as_elem(p.dtype);
+  a.v_type = as_elem(p.dtype);
+  a.o_type = as_elem(out_dtype);
+  return a;
+}
+
+// Stage 2: the group of (tile u, position j) is u*tau + i*b + j, i < m_tau.
+GroupedArgs stage2_args(const monarch_plan_info& p, const void* q, const void* k, const void* y,
+                        int32_t y_dtype, void* out) {
+  GroupedArgs a{};
+  a.q = q; a.k = k; a.v = y; a.o = out;
+  a.head_elems = p.N * p.head_dim;
+  a.heads = static_cast<int32_t>(p.batch * p.heads);
+  a.problems = static_cast<int32_t>(p.tiles * p.b);
+  a.inner = static_cast<int32_t>(p.b);
+  a.outer = p.tau;
+  a.row_stride = p.b;
+  a.L = static_cast<int32_t>(p.m_tau);
+  a.D = static_cast<int32_t>(p.head_dim);
+  a.scale_log2 = p.scale * 1.4426950408889634f;
+  a.qk_type = as_elem(p.dtype);
+  a.v_type = as_elem(y_dtype);
+  a.o_type = as_elem(p.dtype);
+  return a;
+}
+
+int32_t choose_kernel(const GroupedArgs& a, uint32_t flags) {
+  if (!(flags & MONARCH_FLAG_GENERIC)) {
+    if (small_supported(a)) return kKernelSmall;
+    if (flash_supported(a)) return kKernelFlash;
+  }
+  return kKernelGeneric;
+}
+
+hipError_t launch(int32_t kernel, const GroupedArgs& a, hipStream_t s) {
+  switch (kernel) {
+    case kKernelFlash: return launch_flash(a, s);
+    case kKernelSmall: return launch_small(a, s);
+    default: return launch_generic(a, s);
+  }
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
+}
+
+}  // namespace
+
+extern "C" {
+
+monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t heads, int32_t head_dim,
+                                 int32_t T, int32_t H, int32_t W, int32_t align, int64_t custom_b,
+                                 int64_t tile_tokens, int32_t dtype, float scale, uint32_t flags) {
+  if (!out) return MONARCH_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (batch < 1 || heads < 1 || head_dim < 1 || T < 1 || H < 1 || W < 1) return MONARCH_ERR_INVALID_ARG;
+  if (dtype != MONARCH_BF16 && dtype != MONARCH_FP32) return MONARCH_ERR_INVALID_ARG;
+  if (align < MONARCH_ALIGN_FRAME || align > MONARCH_ALIGN_CUSTOM) return MONARCH_ERR_INVALID_ARG;
+  if (flags & ~kKnownFlags) return MONARCH_ERR_INVALID_ARG;
+  if (!isfinite(scale)) return MONARCH_ERR_INVALID_ARG;
+  if (tile_tokens < 0) return MONARCH_ERR_INVALID_ARG;
+  if (head_dim != 64 && head_dim != 128) return MONARCH_ERR_UNSUPPORTED;
+
+  const int64_t N = static_cast<int64_t>(T) * H * W;
+  if (N >= (int64_t{1} << 31)) return MONARCH_ERR_INVALID_ARG;
+  const int64_t BH = static_cast<int64_t>(batch) * heads;
+  if (BH >= (int64_t{1} << 31) || BH * N * head_dim >= (int64_t{1} << 56)) return MONARCH_ERR_INVALID_ARG;
+
+  int64_t b = 0;
+  switch (align) {
+    case MONARCH_ALIGN_FRAME: b = static_cast<int64_t>(H) * W; break;
+    case MONARCH_ALIGN_ROW: b = W; break;
+    case MONARCH_ALIGN_DENSE: b = N; break;
+    case MONARCH_ALIGN_TOKEN: b = 1; break;
+    default:
+      if (custom_b < 1) return MONARCH_ERR_INVALID_ARG;
+      b = custom_b;
+  }
+  if (N % b) return MONARCH_ERR_UNALIGNED;
+  // with (t,h,w) row-major tokens the contiguous splits that keep every axis
+  // inside one block dimension are b in {1, W, H*W, N}
+  const bool axis_aligned = b == 1 || b == W || b == static_cast<int64_t>(H) * W || b == N;
+  if (!axis_aligned && !(flags & MONARCH_FLAG_ALLOW_UNALIGNED)) return MONARCH_ERR_UNALIGNED;
+  const int64_t tau = tile_tokens ? tile_tokens : N;
+  if (tau % b || N % tau) return MONARCH_ERR_UNALIGNED;
+
+  monarch_plan* p = new (std::nothrow) monarch_plan;
+  if (!p) return MONARCH_ERR_INVALID_ARG;
+  monarch_plan_info& i = p->info;
+  i = monarch_plan_info{};
+  i.batch = batch; i.heads = heads; i.head_dim = head_dim;
+  i.T = T; i.H = H; i.W = W; i.N = N;
+  i.b = b; i.tau = tau; i.m_tau = tau / b; i.tiles = N / tau;
+  i.dtype = dtype;
+  i.y_dtype = (dtype == MONARCH_FP32 || (flags & MONARCH_FLAG_Y_FP32)) ? MONARCH_FP32 : MONARCH_BF16;
+  i.scale = scale != 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
+  i.flags = flags;
+  const bool has1 = b > 1, has2 = i.m_tau > 1;
+  i.workspace_bytes = (has1 && has2) ? tensor_bytes(i, i.y_dtype) : 0;
+  i.flops_stage1 = has1 || !has2 ? 4 * BH * N * b * head_dim : 0;
+  i.flops_stage2 = has2 ? 4 * BH * N * i.m_tau * head_dim : 0;
+  // kernel choice is a function of the problem geometry only (no device query)
+  i.stage1_kernel = kKernelNone;
+  i.stage2_kernel = kKernelNone;
+  if (has1 || !has2) {
+    GroupedArgs a = stage1_args(i, nullptr, nullptr, nullptr, nullptr, has2 ? i.y_dtype : dtype);
+    i.stage1_kernel = choose_kernel(a, flags);
+  }
+  if (has2) {
+    GroupedArgs a = stage2_args(i, nullptr, nullptr, nullptr, has1 ? i.y_dtype : dtype, nullptr);
+    i.stage2_kernel = choose_kernel(a, flags);
+  }
+  *out = p;
+  return MONARCH_OK;
+}
+
+void monarch_attn_destroy(monarch_plan* plan) { delete plan; }
+
+size_t monarch_attn_workspace_size(const monarch_plan* plan) {
+  return plan ? static_cast<size_t>(plan->info.workspace_bytes) : 0;
+}
+
+monarch_status monarch_attn_plan_info(const monarch_plan* plan, monarch_plan_info* info) {
+  if (!plan || !info) return MONARCH_ERR_INVALID_ARG;
+  *info = plan->info;
+  return MONARCH_OK;
+}
+
+static monarch_status run_stage1(const monarch_plan_info& p, const void* q, const void* k, const void* v,
+                                 void* y, int32_t y_dtype, hipStream_t s) {
+  GroupedArgs a = stage1_args(p, q, k, v, y, y_dtype);
+  return launch(p.stage1_kernel, a, s) == hipSuccess ? MONARCH_OK : MONARCH_ERR_HIP;
+}
+
+static monarch_status run_stage2(const monarch_plan_info& p, const void* q, const void* k, const void* y,
+                                 int32_t y_dtype, void* o, hipStream_t s) {
+  GroupedArgs a = stage2_args(p, q, k, y, y_dtype, o);
+  return launch(p.stage2_kernel, a, s) == hipSuccess ? MONARCH_OK : MONARCH_ERR_HIP;
+}
+
+monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, const void* k,
+                                    const void* v, void* o, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  if (!plan || !q || !k || !v || !o) return MONARCH_ERR_INVALID_ARG;
+  const monarch_plan_info& p = plan->info;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return MONARCH_ERR_UNALIGNED;
+  const int64_t io = tensor_bytes(p, p.dtype);
+  const int64_t ws = p.workspace_bytes;
+  if (ws > 0) {
+    if (!workspace || static_cast<int64_t>(workspace_bytes) < ws) return MONARCH_ERR_WORKSPACE;
+    if (misaligned(workspace)) return MONARCH_ERR_UNALIGNED;
+  }
+  if (overlap(o, io, q, io) || overlap(o, io, k, io) || overlap(o, io, v, io)) return MONARCH_ERR_ALIAS;
+  if (ws > 0 && (overlap(o, io, workspace, ws) || overlap(workspace, ws, q, io) ||
+                 overlap(workspace, ws, k, io) || overlap(workspace, ws, v, io)))
+    return MONARCH_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool has1 = p.b > 1, has2 = p.m_tau > 1;
+  if (!has2) return run_stage1(p, q, k, v, o, p.dtype, s);  // second factor is the identity
+  if (!has1) return run_stage2(p, q, k, v, p.dtype, o, s);  // first factor is the identity: Y = V
+  monarch_status st = run_stage1(p, q, k, v, workspace, p.y_dtype, s);
+  if (st != MONARCH_OK) return st;
+  return run_stage2(p, q, k, workspace, p.y_dtype, o, s);
+}
+
+monarch_status monarch_attn_stage1(const monarch_plan* plan, const void* q, const void* k,
+                                   const void* v, void* y, size_t y_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !y) return MONARCH_ERR_INVALID_ARG;
+  const monarch_plan_info& p = plan->info;
+  if (p.b == 1) return MONARCH_ERR_INVALID_ARG;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(y)) return MONARCH_ERR_UNALIGNED;
+  const int32_t ydt = p.m_tau > 1 ? p.y_dtype : p.dtype;
+  const int64_t need = tensor_bytes(p, ydt), io = tensor_bytes(p, p.dtype);
+  if (static_cast<int64_t>(y_bytes) < need) return MONARCH_ERR_WORKSPACE;
+  if (overlap(y, need, q, io) || overlap(y, need, k, io) || overlap(y, need, v, io)) return MONARCH_ERR_ALIAS;
+  return run_stage1(p, q, k, v, y, ydt, static_cast<hipStream_t>(stream));
+}
+
+monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, const void* k,
+                                   const void* y, void* o, void* stream) {
+  if (!plan || !q || !k || !y || !o) return MONARCH_ERR_INVALID_ARG;
+  const monarch_plan_info& p = plan->info;
+  if (p.m_tau == 1) return MONARCH_ERR_INVALID_ARG;
+  if (misaligned(q) || misaligned(k) || misaligned(y) || misaligned(o)) return MONARCH_ERR_UNALIGNED;
+  const int32_t ydt = p.b > 1 ? p.y_dtype : p.dtype;
+  const int64_t io = tensor_bytes(p, p.dtype), ny = tensor_bytes(p, ydt);
+  if (overlap(o, io, q, io) || overlap(o, io, k, io) || overlap(o, io, y, ny)) return MONARCH_ERR_ALIAS;
+  return run_stage2(p, q, k, y, ydt, o, static_cast<hipStream_t>(stream));
+}
+
+const char* monarch_status_string(monarch_status status) {
+  switch (status) {
+    case MONARCH_OK: return "ok";
+    case MONARCH_ERR_INVALID_ARG: return "invalid argument";
+    case MONARCH_ERR_UNSUPPORTED: return "unsupported head_dim or dtype";
+    case MONARCH_ERR_UNALIGNED: return "block, tile or pointer alignment violated";
+    case MONARCH_ERR_WORKSPACE: return "workspace missing or too small";
+    case MONARCH_ERR_ALIAS: return "output overlaps an input or the workspace";
+    case MONARCH_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* monarch_attn_kernel_name(int32_t kernel_id) { return kernel_name(kernel_id); }
+
+int32_t monarch_attn_abi_version(void) { return MONARCH_ABI_VERSION; }
+
+}  // extern "C"
+
+namespace monarch {
+const char* kernel_name(int32_t id) {
+  switch (id) {
+    case kKernelNone: return "none";
+    case kKernelGeneric: return "generic_valu_fp32";
+    case kKernelFlash: return "flash_mfma_bf16";
+    case kKernelSmall: return "small_group_mfma_bf16";
+    case kKernelTiny: return "tiny_group_valu";
+  }
+  return "unknown";
+}
+}  // namespace monarch

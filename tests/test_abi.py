@@ -1,0 +1,185 @@
+"""C-ABI checks that need no GPU: exported symbols, plan arithmetic, and every
+validation error path. Pointer arguments here are fake addresses that the
+library must reject before any HIP call; no case reaches a launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+from structured_attention_video_amd import _lib, MonarchPlan, MonarchError
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+L = _lib.lib()
+
+
+def _declared_functions():
+    names = set()
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(monarch_\w+)\s*\(", src))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    declared = _declared_functions()
+    assert declared == set(_lib.EXPORTED)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.monarch_attn_abi_version() == 1
+
+
+def _plan(batch=1, heads=2, d=128, grid=(4, 6, 10), align=0, custom_b=0, tile=0, dtype=0,
+          scale=0.0, flags=0):
+    h = ctypes.c_void_p(123)
+    st = L.monarch_attn_plan(ctypes.byref(h), batch, heads, d, *grid, align, custom_b, tile, dtype,
+                             scale, flags)
+    return st, h
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=0), _lib.ERR_INVALID_ARG),
+    (dict(heads=-1), _lib.ERR_INVALID_ARG),
+    (dict(grid=(0, 6, 10)), _lib.ERR_INVALID_ARG),
+    (dict(dtype=7), _lib.ERR_INVALID_ARG),
+    (dict(align=9), _lib.ERR_INVALID_ARG),
+    (dict(flags=1 << 20), _lib.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), _lib.ERR_INVALID_ARG),
+    (dict(tile=-5), _lib.ERR_INVALID_ARG),
+    (dict(grid=(2048, 1024, 1024)), _lib.ERR_INVALID_ARG),  # N >= 2^31
+    (dict(d=96), _lib.ERR_UNSUPPORTED),
+    (dict(d=256), _lib.ERR_UNSUPPORTED),
+    (dict(align=4, custom_b=0), _lib.ERR_INVALID_ARG),
+    (dict(align=4, custom_b=7), _lib.ERR_UNALIGNED),       # 7 does not divide 240
+    (dict(align=4, custom_b=20), _lib.ERR_UNALIGNED),      # 2W cuts the h axis
+    (dict(tile=100), _lib.ERR_UNALIGNED),                  # not whole frames
+    (dict(tile=180), _lib.ERR_UNALIGNED),                  # 3 frames do not divide 4
+])
+def test_plan_errors(kw, status):
+    st, h = _plan(**kw)
+    assert st == status
+    assert h.value is None
+
+
+def test_plan_null_out():
+    assert L.monarch_attn_plan(None, 1, 1, 64, 2, 2, 2, 0, 0, 0, 0, 0.0, 0) == _lib.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name,b,m_tau,tiles", [
+    ("tiny_fp32", 64, 8, 1),
+    ("frame_bf16", 1560, 21, 1),
+    ("row_bf16", 52, 630, 1),
+    ("tiled_bf16", 1560, 3, 7),
+    ("long_bf16", 1560, 81, 1),
+])
+def test_plan_info_for_the_workloads(name, b, m_tau, tiles):
+    import datagen
+    c = datagen.CONFIGS[name]
+    p = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align=c["align"],
+                    tile_tokens=c["tile_tokens"], dtype=c["dtype"])
+    i = p.info
+    assert (i["b"], i["m_tau"], i["tiles"]) == (b, m_tau, tiles)
+    N = i["N"]
+    assert oracle.block_size(c["grid"], c["align"]) == b
+    want = oracle.flop_count(c["batch"], c["heads"], N, c["d"], b, m_tau)
+    assert i["flops_stage1"] + i["flops_stage2"] == want
+    esz = 4 if c["dtype"] == "fp32" else 2
+    assert p.workspace_bytes == c["batch"] * c["heads"] * N * c["d"] * esz
+    assert abs(i["scale"] - c["d"] ** -0.5) < 1e-7
+    p.close()
+
+
+def test_identity_factors_need_no_workspace():
+    for align, tile in [("dense", 0), ("token", 0), ("frame", 60)]:
+        p = MonarchPlan(1, 1, 64, (4, 6, 10), align=align, tile_tokens=tile, dtype="fp32")
+        assert p.workspace_bytes == 0
+        s1, s2 = p.kernel_names()
+        if align == "token":
+            assert s1 == "none" and s2 != "none"
+        else:
+            assert s2 == "none" and s1 != "none"
+        p.close()
+
+
+def test_custom_unaligned_needs_flag():
+    with pytest.raises(MonarchError):
+        MonarchPlan(1, 1, 64, (4, 6, 10), align="custom", custom_b=20)
+    p = MonarchPlan(1, 1, 64, (4, 6, 10), align="custom", custom_b=20, allow_unaligned=True)
+    assert p.info["b"] == 20 and p.info["m_tau"] == 12
+    # aligned custom sizes need no flag
+    for b in (1, 10, 60, 240):
+        MonarchPlan(1, 1, 64, (4, 6, 10), align="custom", custom_b=b).close()
+
+
+def test_y_fp32_flag():
+    p = MonarchPlan(1, 1, 128, (4, 6, 10), y_fp32=True)
+    assert p.info["y_dtype"] == _lib.FP32 and p.workspace_bytes == 240 * 128 * 4
+
+
+# ------------------------------------------------------------- forward error paths
+A = 0x7f0000000000          # fake, never dereferenced
+STEP = 1 << 24              # far apart: no accidental overlap
+
+
+@pytest.fixture
+def plan():
+    st, h = _plan(heads=2, grid=(4, 6, 10))  # bf16, N = 240, d = 128
+    assert st == _lib.OK
+    yield h
+    L.monarch_attn_destroy(h)
+
+
+def _fwd(h, q=A, k=A + STEP, v=A + 2 * STEP, o=A + 3 * STEP, ws=A + 4 * STEP, ws_n=1 << 30):
+    return L.monarch_attn_forward(h, q, k, v, o, ws, ws_n, None)
+
+
+def test_forward_errors(plan):
+    io = 2 * 240 * 128 * 2
+    assert _fwd(None) == _lib.ERR_INVALID_ARG
+    assert _fwd(plan, q=None) == _lib.ERR_INVALID_ARG
+    assert _fwd(plan, o=None) == _lib.ERR_INVALID_ARG
+    assert _fwd(plan, k=A + STEP + 2) == _lib.ERR_UNALIGNED
+    assert _fwd(plan, ws=None) == _lib.ERR_WORKSPACE
+    assert _fwd(plan, ws_n=io - 1) == _lib.ERR_WORKSPACE
+    assert _fwd(plan, ws=A + 4 * STEP + 8) == _lib.ERR_UNALIGNED
+    assert _fwd(plan, o=A + 16) == _lib.ERR_ALIAS                    # o overlaps q
+    assert _fwd(plan, o=A + 2 * STEP + io - 16) == _lib.ERR_ALIAS    # o tail overlaps v
+    assert _fwd(plan, ws=A + 3 * STEP + 64) == _lib.ERR_ALIAS        # workspace overlaps o
+    assert _fwd(plan, ws=A + STEP) == _lib.ERR_ALIAS                 # workspace overlaps k
+
+
+def test_stage_entry_errors(plan):
+    io = 2 * 240 * 128 * 2
+    assert L.monarch_attn_stage1(plan, A, A + STEP, A + 2 * STEP, None, io, None) == _lib.ERR_INVALID_ARG
+    assert L.monarch_attn_stage1(plan, A, A + STEP, A + 2 * STEP, A + 3 * STEP, io - 2, None) == _lib.ERR_WORKSPACE
+    assert L.monarch_attn_stage1(plan, A, A + STEP, A + 2 * STEP, A + 2 * STEP, io, None) == _lib.ERR_ALIAS
+    assert L.monarch_attn_stage2(plan, A, A + STEP, A + 2 * STEP, A + 2 * STEP + 32, None) == _lib.ERR_ALIAS
+    assert L.monarch_attn_stage2(plan, A, A + STEP, A + 2 * STEP + 4, A + 3 * STEP, None) == _lib.ERR_UNALIGNED
+    st, dense = _plan(grid=(4, 6, 10), align=2)
+    assert L.monarch_attn_stage2(dense, A, A + STEP, A + 2 * STEP, A + 3 * STEP, None) == _lib.ERR_INVALID_ARG
+    L.monarch_attn_destroy(dense)
+    st, tok = _plan(grid=(4, 6, 10), align=3)
+    assert L.monarch_attn_stage1(tok, A, A + STEP, A + 2 * STEP, A + 3 * STEP, io, None) == _lib.ERR_INVALID_ARG
+    L.monarch_attn_destroy(tok)
+
+
+def test_status_strings_and_kernel_names():
+    for code in range(7):
+        assert L.monarch_status_string(code)
+    assert L.monarch_status_string(99) == b"unknown status"
+    for kid in range(6):
+        assert L.monarch_attn_kernel_name(kid)
+    assert L.monarch_attn_plan_info(None, None) == _lib.ERR_INVALID_ARG
+    assert L.monarch_attn_workspace_size(None) == 0
+    L.monarch_attn_destroy(None)
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    p = MonarchPlan(1, 1, 64, (2, 2, 2), dtype="fp32")
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        p.forward(x, x, x)
