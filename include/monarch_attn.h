@@ -103,7 +103,8 @@ typedef struct monarch_plan_info {
  *   align        monarch_align; custom_b is read only for MONARCH_ALIGN_CUSTOM.
  *   tile_tokens  0 = untiled (tau = N); else tau, a multiple of b dividing N
  *                (explainer section 2.B: each large block cut into sub-blocks).
- *   dtype        monarch_dtype; scale 0 = 1/sqrt(head_dim); flags MONARCH_FLAG_*. */
+ *   dtype        monarch_dtype; scale 0 = 1/sqrt(head_dim), else a positive finite softmax
+ *                scale (negative or non-finite: MONARCH_ERR_INVALID_ARG); flags MONARCH_FLAG_*. */
 monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t heads, int32_t head_dim,
                                  int32_t T, int32_t H, int32_t W, int32_t align, int64_t custom_b,
                                  int64_t tile_tokens, int32_t dtype, float scale, uint32_t flags);

@@ -1,9 +1,388 @@
-// bf16 MFMA grouped-attention kernels (placeholder until the MFMA path lands).
-#include "internal.h"
+// bf16 MFMA grouped-attention kernels for gfx950.
+//
+// flash: problems longer than 128 rows (stage-1 frame blocks, stage-2 groups
+//   of many blocks, dense attention). A workgroup of four waves owns 128
+//   query rows of one problem (32 per wave, kept as MFMA B operands in
+//   registers) and streams the problem's keys and values in tiles of 64 rows
+//   through double-buffered LDS: the next tile's global loads are in flight
+//   while the current tile is multiplied. Softmax is online with a lazy
+//   rescale: the running maximum only moves when a tile's maximum exceeds it
+//   by more than 8 (log2 units), so the unnormalised weights stay <= 2^8 and
+//   the accumulator is rescaled rarely. Workgroups are ordered so that the
+//   query tiles of one problem land on the same XCD and share its L2.
+//
+// group: problems of at most 128 rows (stage-2 groups of a few blocks,
+//   stage-1 row blocks). One pass: a workgroup loads whole problems (K and
+//   V^T) into LDS once; each wave owns 32 query rows of one problem.
+//
+// The softmax follows the "SRAM reduction" design the MonarchRT pages
+// describe for their kernels (gist.science explainer, section 2.C): scores
+// never leave the chip and memory stays linear in N.
+#include "mfma_common.h"
 
 namespace monarch {
-bool flash_supported(const GroupedArgs&) { return false; }
-hipError_t launch_flash(const GroupedArgs&, hipStream_t) { return hipErrorInvalidValue; }
-bool small_supported(const GroupedArgs&) { return false; }
-hipError_t launch_small(const GroupedArgs&, hipStream_t) { return hipErrorInvalidValue; }
+namespace {
+
+using namespace mfma;
+
+constexpr float kRescaleThreshold = 8.0f;
+
+struct Rows {
+  int64_t head_elems;
+  int64_t base;   // first token of the problem
+  int64_t rs;     // token stride between rows
+};
+
+__device__ __forceinline__ int64_t problem_base(const GroupedArgs& a, int p) {
+  return static_cast<int64_t>(p / a.inner) * a.outer + (p % a.inner);
+}
+
+// Map the hardware workgroup id to a logical id so that consecutive logical
+// ids run on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
+__device__ __forceinline__ int xcd_order(int w, int nwg) {
+  const int q = nwg >> 3, r = nwg & 7, x = w & 7, slot = w >> 3;
+  return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
+}
+
+// Load one 32-row query fragment (rows row0 .. row0+31, clamped to L) as
+// MFMA B operands.
+template <int D>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const bf16* q, const Rows& r, int row0, int L,
+                                       int lane) {
+  const int row = row0 + (lane & 31);
+  const bool ok = row < L;
+  const bf16* src = q + (r.base + static_cast<int64_t>(ok ? row : 0) * r.rs) * D + (lane >> 5) * 8;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    u32x4 v = ok ? ld16(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// ---------------------------------------------------------------- flash
+constexpr int FBM = 128;  // query rows per workgroup
+constexpr int FBN = 64;   // keys per LDS tile
+constexpr int FNT = 256;  // threads
+
+template <int D>
+struct FlashLds {
+  static constexpr int kbytes = FBN * KRow<D>::bytes;
+  static constexpr int vbytes = D * VRow<FBN>::bytes;
+  static constexpr int buf = kbytes + vbytes;
+  static constexpr int kchunks = FBN * D / 8 / FNT;  // 16-byte K chunks per thread
+  static constexpr int vunits = 16 * (D / 8);        // (4 keys x 8 channels) units per tile
+};
+
+template <int D>
+struct FlashRegs {
+  u32x4 k[FlashLds<D>::kchunks];
+  u32x4 v[4];
+};
+
+template <int D>
+__device__ __forceinline__ void flash_load(FlashRegs<D>& g, const bf16* kp, const bf16* vp, const Rows& r,
+                                           int key0, int L, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int c = 0; c < FlashLds<D>::kchunks; ++c) {
+    const int id = tid + FNT * c;
+    const int row = id / CPR, ch = id % CPR;
+    const int key = key0 + row;
+    g.k[c] = key < L ? ld16(kp + (r.base + static_cast<int64_t>(key) * r.rs) * D + ch * 8)
+                     : u32x4{0u, 0u, 0u, 0u};
+  }
+  if (tid < FlashLds<D>::vunits) {
+    const int kg = tid & 15, dc = tid >> 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = key0 + 4 * kg + j;
+      g.v[j] = key < L ? ld16(vp + (r.base + static_cast<int64_t>(key) * r.rs) * D + dc * 8)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void flash_store(char* buf, const FlashRegs<D>& g, int tid) {
+  constexpr int CPR = D / 8;
+  char* kl = buf;
+  char* vt = buf + FlashLds<D>::kbytes;
+#pragma unroll
+  for (int c = 0; c < FlashLds<D>::kchunks; ++c) {
+    const int id = tid + FNT * c;
+    const int row = id / CPR, ch = id % CPR;
+    *reinterpret_cast<u32x4*>(kl + row * KRow<D>::bytes + ch * 16) = g.k[c];
+  }
+  if (tid < FlashLds<D>::vunits) {
+    const int kg = tid & 15, dc = tid >> 4;
+    store_vt4<FBN>(vt, dc * 8, key_slot(4 * kg), g.v[0], g.v[1], g.v[2], g.v[3]);
+  }
+}
+
+// One 64-key tile for one wave: scores, online softmax, PV.
+template <int D>
+__device__ __forceinline__ void flash_tile(const char* buf, const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
+                                           float& m, float& l, int nvalid, float c, int lane) {
+  const char* kl = buf;
+  const char* vt = buf + FlashLds<D>::kbytes;
+  const int h = lane >> 5;
+  const bool two = nvalid > 32;
+  f32x16 s[2];
+  s[0] = scores_tile<D>(kl, 0, qf, lane);
+  if (two) s[1] = scores_tile<D>(kl, 32, qf, lane);
+  if (nvalid < FBN) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (32 * t + acc_key(i, h) >= nvalid) s[t][i] = -INFINITY;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+  if (two) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
+  }
+  mx = halves_max(mx) * c;
+  if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = fast_exp2(m - mn);
+    l *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
+    m = mn;
+  }
+  f32x16 p[2];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    p[0][i] = fast_exp2(fmaf(s[0][i], c, -m));
+    l += p[0][i];
+  }
+  if (two) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[1][i] = fast_exp2(fmaf(s[1][i], c, -m));
+      l += p[1][i];
+    }
+  }
+  const int steps = two ? 4 : 2;
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    if (st < steps) {
+      const bf16x8 pb = p_operand(p[st >> 1], st & 1);
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) o[mt] = pv_step<FBN>(vt, mt, st, pb, o[mt], lane);
+    }
+  }
+}
+
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles, int nwg) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * FlashLds<D>::buf];
+  const int id = xcd_order(blockIdx.x, nwg);
+  const int qt = id % qtiles;
+  const int rest = id / qtiles;
+  const int p = rest % a.problems;
+  const int hd = rest / a.problems;
+
+  Rows r;
+  r.head_elems = a.head_elems;
+  r.base = problem_base(a, p);
+  r.rs = a.row_stride;
+  const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
+  const bf16* qp = static_cast<const bf16*>(a.q) + hoff;
+  const bf16* kp = static_cast<const bf16*>(a.k) + hoff;
+  const bf16* vp = static_cast<const bf16*>(a.v) + hoff;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = a.L;
+  const int row0 = qt * FBM + wave * 32;
+  const bool active = row0 < L;
+
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, qp, r, row0, L, lane);
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
+  float m = -INFINITY, l = 0.f;
+  const float c = a.scale_log2;
+
+  const int ntiles = (L + FBN - 1) / FBN;
+  FlashRegs<D> g;
+  flash_load<D>(g, kp, vp, r, 0, L, tid);
+  flash_store<D>(smem, g, tid);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) flash_load<D>(g, kp, vp, r, (t + 1) * FBN, L, tid);
+    if (active) flash_tile<D>(smem + (t & 1) * FlashLds<D>::buf, qf, o, m, l, min(FBN, L - t * FBN), c, lane);
+    if (more) flash_store<D>(smem + ((t + 1) & 1) * FlashLds<D>::buf, g, tid);
+    __syncthreads();
+  }
+
+  if (!active) return;
+  const float inv = 1.f / halves_sum(l);  // both lane halves of a row are active together
+  const int row = row0 + (lane & 31);
+  if (row < L) store_out<D, OUT_F32>(a.o, hoff + (r.base + static_cast<int64_t>(row) * r.rs) * D, o, inv, lane);
+}
+
+// ---------------------------------------------------------------- group
+template <int D, int QT>
+struct GroupLds {
+  static constexpr int BN = 32 * QT;
+  static constexpr int PPW = QT == 1 ? 4 : (QT == 2 ? 2 : 1);
+  static constexpr int NT = 64 * QT * PPW;
+  static constexpr int kbytes = BN * KRow<D>::bytes;
+  static constexpr int vbytes = D * VRow<BN>::bytes;
+  static constexpr int prob = kbytes + vbytes;
+};
+
+template <int D, int QT, bool OUT_F32>
+__global__ void __launch_bounds__((GroupLds<D, QT>::NT), 2) group_kernel(GroupedArgs a, int wg_per_head) {
+  using G = GroupLds<D, QT>;
+  constexpr int BN = G::BN, PPW = G::PPW, NT = G::NT, CPR = D / 8;
+  __shared__ __attribute__((aligned(16))) char smem[PPW * G::prob];
+
+  const int hd = blockIdx.x / wg_per_head;
+  const int p0 = (blockIdx.x % wg_per_head) * PPW;
+  const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
+  const bf16* qp = static_cast<const bf16*>(a.q) + hoff;
+  const bf16* kp = static_cast<const bf16*>(a.k) + hoff;
+  const bf16* vp = static_cast<const bf16*>(a.v) + hoff;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int L = a.L;
+
+  // K rows: PPW problems x BN rows x CPR chunks
+  for (int id = tid; id < PPW * BN * CPR; id += NT) {
+    const int pl = id / (BN * CPR), row = (id / CPR) % BN, ch = id % CPR;
+    const int p = p0 + pl;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (p < a.problems && row < L)
+      v = ld16(kp + (problem_base(a, p) + static_cast<int64_t>(row) * a.row_stride) * D + ch * 8);
+    *reinterpret_cast<u32x4*>(smem + pl * G::prob + row * KRow<D>::bytes + ch * 16) = v;
+  }
+  // V^T: units of 4 keys x 8 channels; channel chunk fastest so that 16
+  // lanes read one 256-byte row
+  for (int id = tid; id < PPW * (BN / 4) * CPR; id += NT) {
+    const int dc = id % CPR, kg = (id / CPR) % (BN / 4), pl = id / (CPR * (BN / 4));
+    const int p = p0 + pl;
+    u32x4 rows[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int key = 4 * kg + j;
+      rows[j] = (p < a.problems && key < L)
+                    ? ld16(vp + (problem_base(a, p) + static_cast<int64_t>(key) * a.row_stride) * D + dc * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+    store_vt4<BN>(smem + pl * G::prob + G::kbytes, dc * 8, key_slot(4 * kg), rows[0], rows[1], rows[2], rows[3]);
+  }
+  __syncthreads();
+
+  const int pl = wave / QT, qt = wave % QT;
+  const int p = p0 + pl;
+  const int row0 = qt * 32;
+  if (p >= a.problems || row0 >= L) return;
+  Rows r;
+  r.head_elems = a.head_elems;
+  r.base = problem_base(a, p);
+  r.rs = a.row_stride;
+  bf16x8 qf[D / 16];
+  load_q<D>(qf, qp, r, row0, L, lane);
+  const char* kl = smem + pl * G::prob;
+  const char* vt = kl + G::kbytes;
+  const int h = lane >> 5;
+  const float c = a.scale_log2;
+
+  f32x16 s[QT];
+#pragma unroll
+  for (int t = 0; t < QT; ++t) s[t] = scores_tile<D>(kl, 32 * t, qf, lane);
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < QT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      if (32 * t + acc_key(i, h) >= L) s[t][i] = -INFINITY;
+      mx = fmaxf(mx, s[t][i]);
+    }
+  mx = halves_max(mx) * c;
+  float l = 0.f;
+#pragma unroll
+  for (int t = 0; t < QT; ++t)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[t][i] = fast_exp2(fmaf(s[t][i], c, -mx));
+      l += s[t][i];
+    }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < 2 * QT; ++st) {
+    const bf16x8 pb = p_operand(s[st >> 1], st & 1);
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) o[mt] = pv_step<BN>(vt, mt, st, pb, o[mt], lane);
+  }
+  const float inv = 1.f / halves_sum(l);
+  const int row = row0 + (lane & 31);
+  if (row < L) store_out<D, OUT_F32>(a.o, hoff + (r.base + static_cast<int64_t>(row) * r.rs) * D, o, inv, lane);
+}
+
+bool mfma_types_ok(const GroupedArgs& a) {
+  return (a.D == 64 || a.D == 128) && a.qk_type == kBF16 && a.v_type == kBF16;
+}
+
+template <int D, bool F32>
+hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
+  const int qtiles = (a.L + FBM - 1) / FBM;
+  const int64_t nwg = static_cast<int64_t>(qtiles) * a.problems * a.heads;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((flash_kernel<D, F32>), dim3(static_cast<unsigned>(nwg)), dim3(FNT), 0, s, a, qtiles,
+                     static_cast<int>(nwg));
+  return hipGetLastError();
+}
+
+template <int D, int QT, bool F32>
+hipError_t launch_group_t(const GroupedArgs& a, hipStream_t s) {
+  using G = GroupLds<D, QT>;
+  const int wg_per_head = (a.problems + G::PPW - 1) / G::PPW;
+  const int64_t nwg = static_cast<int64_t>(wg_per_head) * a.heads;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((group_kernel<D, QT, F32>), dim3(static_cast<unsigned>(nwg)), dim3(G::NT), 0, s, a,
+                     wg_per_head);
+  return hipGetLastError();
+}
+
+template <int D, bool F32>
+hipError_t launch_group_d(const GroupedArgs& a, hipStream_t s) {
+  const int qt = (a.L + 31) / 32;
+  switch (qt) {
+    case 1: return launch_group_t<D, 1, F32>(a, s);
+    case 2: return launch_group_t<D, 2, F32>(a, s);
+    case 3: return launch_group_t<D, 3, F32>(a, s);
+    case 4: return launch_group_t<D, 4, F32>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool flash_supported(const GroupedArgs& a) { return mfma_types_ok(a) && a.L > 128; }
+
+hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
+  if (!flash_supported(a)) return hipErrorInvalidValue;
+  const bool f32 = a.o_type == kF32;
+  if (a.D == 128) return f32 ? launch_flash_t<128, true>(a, s) : launch_flash_t<128, false>(a, s);
+  return f32 ? launch_flash_t<64, true>(a, s) : launch_flash_t<64, false>(a, s);
+}
+
+bool small_supported(const GroupedArgs& a) { return mfma_types_ok(a) && a.L >= 2 && a.L <= 128; }
+
+hipError_t launch_small(const GroupedArgs& a, hipStream_t s) {
+  if (!small_supported(a)) return hipErrorInvalidValue;
+  const bool f32 = a.o_type == kF32;
+  if (a.D == 128) return f32 ? launch_group_d<128, true>(a, s) : launch_group_d<128, false>(a, s);
+  return f32 ? launch_group_d<64, true>(a, s) : launch_group_d<64, false>(a, s);
+}
+
 }  // namespace monarch

@@ -104,7 +104,7 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
   if (dtype != MONARCH_BF16 && dtype != MONARCH_FP32) return MONARCH_ERR_INVALID_ARG;
   if (align < MONARCH_ALIGN_FRAME || align > MONARCH_ALIGN_CUSTOM) return MONARCH_ERR_INVALID_ARG;
   if (flags & ~kKnownFlags) return MONARCH_ERR_INVALID_ARG;
-  if (!isfinite(scale)) return MONARCH_ERR_INVALID_ARG;
+  if (!isfinite(scale) || scale < 0.f) return MONARCH_ERR_INVALID_ARG;
   if (tile_tokens < 0) return MONARCH_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return MONARCH_ERR_UNSUPPORTED;
 

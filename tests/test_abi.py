@@ -48,6 +48,7 @@ def _plan(batch=1, heads=2, d=128, grid=(4, 6, 10), align=0, custom_b=0, tile=0,
     (dict(align=9), _lib.ERR_INVALID_ARG),
     (dict(flags=1 << 20), _lib.ERR_INVALID_ARG),
     (dict(scale=float("nan")), _lib.ERR_INVALID_ARG),
+    (dict(scale=-0.5), _lib.ERR_INVALID_ARG),
     (dict(tile=-5), _lib.ERR_INVALID_ARG),
     (dict(grid=(2048, 1024, 1024)), _lib.ERR_INVALID_ARG),  # N >= 2^31
     (dict(d=96), _lib.ERR_UNSUPPORTED),
