@@ -27,6 +27,11 @@ FLAGS = [
 ]
 
 
+# Kernel sources only: no NaN-quieting around min/max (IEEE mode off). The
+# C-ABI source keeps strict IEEE semantics for its argument checks.
+KERNEL_FLAGS = ["-mno-amdgpu-ieee", "-fno-honor-nans"]
+
+
 def hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -39,7 +44,8 @@ def sources():
 
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [hipcc(), *FLAGS, "-c", src, "-o", obj]
+    extra = KERNEL_FLAGS if os.path.basename(src).startswith("kernel_") else []
+    cmd = [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(x for x in r.stderr.splitlines() if "packed-fp32-ops" not in x)
     if r.returncode != 0:

@@ -49,14 +49,11 @@ __device__ __forceinline__ int xcd_order(int w, int nwg) {
 template <int D>
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[D / 16], const bf16* q, const Rows& r, int row0, int L,
                                        int lane) {
-  const int row = row0 + (lane & 31);
-  const bool ok = row < L;
-  const bf16* src = q + (r.base + static_cast<int64_t>(ok ? row : 0) * r.rs) * D + (lane >> 5) * 8;
+  // rows past the end are clamped to the last row; their outputs are never stored
+  const int row = min(row0 + (lane & 31), L - 1);
+  const bf16* src = q + (r.base + static_cast<int64_t>(row) * r.rs) * D + (lane >> 5) * 8;
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    u32x4 v = ok ? ld16(src + ks * 16) : u32x4{0u, 0u, 0u, 0u};
-    qf[ks] = __builtin_bit_cast(bf16x8, v);
-  }
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, ld16(src + ks * 16));
 }
 
 // ---------------------------------------------------------------- flash
@@ -64,86 +61,124 @@ constexpr int FBM = 128;  // query rows per workgroup
 constexpr int FBN = 64;   // keys per LDS tile
 constexpr int FNT = 256;  // threads
 
+// LDS: two-slot rings for K tiles and V^T tiles. Iteration j multiplies
+// Q K_{j+1}^T (scores one tile ahead) and V_j^T P_j^T, while tile K_{j+2} and
+// V_{j+1} are in flight from global memory into registers; they are written
+// into the slots of K_j and V_{j-1}, which no wave reads any more.
 template <int D>
 struct FlashLds {
   static constexpr int kbytes = FBN * KRow<D>::bytes;
   static constexpr int vbytes = D * VRow<FBN>::bytes;
-  static constexpr int buf = kbytes + vbytes;
+  static constexpr int total = 2 * kbytes + 2 * vbytes;
   static constexpr int kchunks = FBN * D / 8 / FNT;  // 16-byte K chunks per thread
   static constexpr int vunits = 16 * (D / 8);        // (4 keys x 8 channels) units per tile
 };
 
+// Global loads go through buffer descriptors that cover exactly one
+// problem's rows (base = its first token, size = up to the end of its last
+// row): a row past the end of the problem reads as zeros, so tail tiles need
+// no clamp or branch. Keys beyond the end are masked out of the softmax and
+// zero values add nothing.
+// The descriptor fields are wave-uniform; readfirstlane tells the compiler so
+// (otherwise it may keep them in vector registers and serialise each load).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t problem_rsrc(const bf16* head, const Rows& r, int L, int D) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(head + r.base * D);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
+  const uint32_t bytes = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(((static_cast<int64_t>(L) - 1) * r.rs + 1) * D * 2));
+  void* base = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(base, static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, static_cast<int>(off), 0, 0));
+}
+
+// Per-thread byte offsets of the 16-byte K chunks inside a tile (tile 0)
 template <int D>
-struct FlashRegs {
-  u32x4 k[FlashLds<D>::kchunks];
-  u32x4 v[4];
+struct KOffsets {
+  uint32_t off[FlashLds<D>::kchunks];
+  __device__ __forceinline__ KOffsets(int tid, int64_t rs) {
+    constexpr int CPR = D / 8;
+#pragma unroll
+    for (int c = 0; c < FlashLds<D>::kchunks; ++c) {
+      const int id = tid + FNT * c;
+      off[c] = static_cast<uint32_t>(((id / CPR) * rs * D + (id % CPR) * 8) * 2);
+    }
+  }
 };
 
 template <int D>
-__device__ __forceinline__ void flash_load(FlashRegs<D>& g, const bf16* kp, const bf16* vp, const Rows& r,
-                                           int key0, int L, int tid) {
+__device__ __forceinline__ void load_k(u32x4 (&g)[FlashLds<D>::kchunks], __amdgpu_buffer_rsrc_t rk,
+                                       const KOffsets<D>& ko, uint32_t tile_off) {
+#pragma unroll
+  for (int c = 0; c < FlashLds<D>::kchunks; ++c) g[c] = bload16(rk, ko.off[c] + tile_off);
+}
+
+template <int D>
+__device__ __forceinline__ void store_k(char* kl, const u32x4 (&g)[FlashLds<D>::kchunks], int tid) {
   constexpr int CPR = D / 8;
 #pragma unroll
   for (int c = 0; c < FlashLds<D>::kchunks; ++c) {
     const int id = tid + FNT * c;
-    const int row = id / CPR, ch = id % CPR;
-    const int key = key0 + row;
-    g.k[c] = key < L ? ld16(kp + (r.base + static_cast<int64_t>(key) * r.rs) * D + ch * 8)
-                     : u32x4{0u, 0u, 0u, 0u};
+    *reinterpret_cast<u32x4*>(kl + (id / CPR) * KRow<D>::bytes + (id % CPR) * 16) = g[c];
   }
+}
+
+// V: thread (kg, dc) loads keys 4kg..4kg+3, channels 8dc..8dc+7
+template <int D>
+__device__ __forceinline__ uint32_t v_offset(int tid, int64_t rs) {
+  const int kg = tid & 15, dc = tid >> 4;
+  return static_cast<uint32_t>((4 * kg * rs * D + dc * 8) * 2);
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(u32x4 (&g)[4], __amdgpu_buffer_rsrc_t rv, uint32_t voff, uint32_t row_bytes,
+                                       uint32_t tile_off, int tid) {
   if (tid < FlashLds<D>::vunits) {
-    const int kg = tid & 15, dc = tid >> 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = key0 + 4 * kg + j;
-      g.v[j] = key < L ? ld16(vp + (r.base + static_cast<int64_t>(key) * r.rs) * D + dc * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int j = 0; j < 4; ++j) g[j] = bload16(rv, voff + tile_off + j * row_bytes);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void flash_store(char* buf, const FlashRegs<D>& g, int tid) {
-  constexpr int CPR = D / 8;
-  char* kl = buf;
-  char* vt = buf + FlashLds<D>::kbytes;
-#pragma unroll
-  for (int c = 0; c < FlashLds<D>::kchunks; ++c) {
-    const int id = tid + FNT * c;
-    const int row = id / CPR, ch = id % CPR;
-    *reinterpret_cast<u32x4*>(kl + row * KRow<D>::bytes + ch * 16) = g.k[c];
-  }
+__device__ __forceinline__ void store_v(char* vt, const u32x4 (&g)[4], int tid) {
   if (tid < FlashLds<D>::vunits) {
     const int kg = tid & 15, dc = tid >> 4;
-    store_vt4<FBN>(vt, dc * 8, key_slot(4 * kg), g.v[0], g.v[1], g.v[2], g.v[3]);
+    store_vt4<FBN>(vt, dc * 8, key_slot(4 * kg), g[0], g[1], g[2], g[3]);
   }
 }
 
-// One 64-key tile for one wave: scores, online softmax, PV.
+// S^T for a 64-key tile: two independent 32-key accumulator chains
 template <int D>
-__device__ __forceinline__ void flash_tile(const char* buf, const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32],
-                                           float& m, float& l, int nvalid, float c, int lane) {
-  const char* kl = buf;
-  const char* vt = buf + FlashLds<D>::kbytes;
-  const int h = lane >> 5;
-  const bool two = nvalid > 32;
-  f32x16 s[2];
-  s[0] = scores_tile<D>(kl, 0, qf, lane);
-  if (two) s[1] = scores_tile<D>(kl, 32, qf, lane);
-  if (nvalid < FBN) {
+__device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const bf16x8 (&qf)[D / 16], int lane) {
+  constexpr int KR = KRow<D>::bytes;
+  const char* r0 = kl + (lane & 31) * KR + (lane >> 5) * 16;
+  const char* r1 = r0 + 32 * KR;
+  s[0] = f32x16{};
+  s[1] = f32x16{};
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        if (32 * t + acc_key(i, h) >= nvalid) s[t][i] = -INFINITY;
+  for (int ks = 0; ks < D / 16; ++ks) {
+    s[0] = mma(ld_bf16x8(r0 + ks * 32), qf[ks], s[0]);
+    s[1] = mma(ld_bf16x8(r1 + ks * 32), qf[ks], s[1]);
   }
-  float mx = s[0][0];
+}
+
+__device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int nvalid, int h) {
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
-  if (two) {
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-  }
+    for (int i = 0; i < 16; ++i)
+      if (32 * t + acc_key(i, h) >= nvalid) s[t][i] = -INFINITY;
+}
+
+// Running max update with lazy rescale of the accumulator.
+template <int D>
+__device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m, float& l, float c) {
+  float mx = fmaxf(s[0][0], s[1][0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
   mx = halves_max(mx) * c;
   if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold)) {
     const float mn = fmaxf(m, mx);
@@ -153,33 +188,40 @@ __device__ __forceinline__ void flash_tile(const char* buf, const bf16x8 (&qf)[D
     for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
     m = mn;
   }
-  f32x16 p[2];
+}
+
+// exp2(s*c - m) as bf16 B operands for the four 16-key PV steps; adds the
+// unnormalised weights to l.
+__device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float c, float m) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    p[0][i] = fast_exp2(fmaf(s[0][i], c, -m));
-    l += p[0][i];
-  }
-  if (two) {
+  for (int st = 0; st < 4; ++st) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p[1][i] = fast_exp2(fmaf(s[1][i], c, -m));
-      l += p[1][i];
+    for (int e = 0; e < 8; ++e) {
+      const float p = fast_exp2(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m));
+      l += p;
+      pb[st][e] = static_cast<bf16>(p);
     }
   }
-  const int steps = two ? 4 : 2;
+}
+
+template <int D>
+__device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vt, const bf16x8 (&pb)[4], int steps, int lane) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     if (st < steps) {
-      const bf16x8 pb = p_operand(p[st >> 1], st & 1);
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) o[mt] = pv_step<FBN>(vt, mt, st, pb, o[mt], lane);
+      for (int mt = 0; mt < D / 32; ++mt) o[mt] = pv_step<FBN>(vt, mt, st, pb[st], o[mt], lane);
     }
   }
 }
 
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles, int nwg) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * FlashLds<D>::buf];
+  using FL = FlashLds<D>;
+  __shared__ __attribute__((aligned(16))) char smem[FL::total];
+  char* const kring = smem;
+  char* const vring = smem + 2 * FL::kbytes;
+
   const int id = xcd_order(blockIdx.x, nwg);
   const int qt = id % qtiles;
   const int rest = id / qtiles;
@@ -195,10 +237,13 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
   const bf16* kp = static_cast<const bf16*>(a.k) + hoff;
   const bf16* vp = static_cast<const bf16*>(a.v) + hoff;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int L = a.L;
   const int row0 = qt * FBM + wave * 32;
   const bool active = row0 < L;
+  const int n = (L + FBN - 1) / FBN;
+  const int nv_last = L - (n - 1) * FBN;
+  const float c = a.scale_log2;
 
   bf16x8 qf[D / 16];
   load_q<D>(qf, qp, r, row0, L, lane);
@@ -206,22 +251,55 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
   float m = -INFINITY, l = 0.f;
-  const float c = a.scale_log2;
 
-  const int ntiles = (L + FBN - 1) / FBN;
-  FlashRegs<D> g;
-  flash_load<D>(g, kp, vp, r, 0, L, tid);
-  flash_store<D>(smem, g, tid);
+  const __amdgpu_buffer_rsrc_t rk = problem_rsrc(kp, r, L, D);
+  const __amdgpu_buffer_rsrc_t rv = problem_rsrc(vp, r, L, D);
+  const KOffsets<D> ko(tid, r.rs);
+  const uint32_t voff = v_offset<D>(tid, r.rs);
+  const uint32_t row_bytes = static_cast<uint32_t>(r.rs * D * 2);
+  const uint32_t tile_bytes = static_cast<uint32_t>(FBN * r.rs * D * 2);
+
+  u32x4 gk[FL::kchunks], gv[4];
+  load_k<D>(gk, rk, ko, 0);
+  load_v<D>(gv, rv, voff, row_bytes, 0, tid);
+  store_k<D>(kring, gk, tid);
+  store_v<D>(vring, gv, tid);
+  if (n > 1) {
+    load_k<D>(gk, rk, ko, tile_bytes);
+    store_k<D>(kring + FL::kbytes, gk, tid);
+  }
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    const bool more = t + 1 < ntiles;
-    if (more) flash_load<D>(g, kp, vp, r, (t + 1) * FBN, L, tid);
-    if (active) flash_tile<D>(smem + (t & 1) * FlashLds<D>::buf, qf, o, m, l, min(FBN, L - t * FBN), c, lane);
-    if (more) flash_store<D>(smem + ((t + 1) & 1) * FlashLds<D>::buf, g, tid);
+
+  f32x16 s[2];
+  if (active) scores64<D>(s, kring, qf, lane);
+
+  // steady state: every iteration has a next tile
+  for (int j = 0; j + 1 < n; ++j) {
+    if (j + 2 < n) load_k<D>(gk, rk, ko, (j + 2) * tile_bytes);
+    load_v<D>(gv, rv, voff, row_bytes, (j + 1) * tile_bytes, tid);
+    if (active) {
+      update_max<D>(s, o, m, l, c);
+      f32x16 sn[2];
+      scores64<D>(sn, kring + ((j + 1) & 1) * FL::kbytes, qf, lane);
+      bf16x8 pb[4];
+      probs(s, pb, l, c, m);
+      pv64<D>(o, vring + (j & 1) * FL::vbytes, pb, 4, lane);
+      s[0] = sn[0];
+      s[1] = sn[1];
+    }
+    if (j + 2 < n) store_k<D>(kring + (j & 1) * FL::kbytes, gk, tid);
+    store_v<D>(vring + ((j + 1) & 1) * FL::vbytes, gv, tid);
     __syncthreads();
   }
 
   if (!active) return;
+  // last tile: mask keys past the end, skip the empty half of the PV product
+  if (nv_last < FBN) mask_tail(s, nv_last, h);
+  update_max<D>(s, o, m, l, c);
+  bf16x8 pb[4];
+  probs(s, pb, l, c, m);
+  pv64<D>(o, vring + ((n - 1) & 1) * FL::vbytes, pb, nv_last > 32 ? 4 : 2, lane);
+
   const float inv = 1.f / halves_sum(l);  // both lane halves of a row are active together
   const int row = row0 + (lane & 31);
   if (row < L) store_out<D, OUT_F32>(a.o, hoff + (r.base + static_cast<int64_t>(row) * r.rs) * D, o, inv, lane);
@@ -367,7 +445,11 @@ hipError_t launch_group_d(const GroupedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool flash_supported(const GroupedArgs& a) { return mfma_types_ok(a) && a.L > 128; }
+// 32-bit buffer offsets must reach one tile past the end of a problem
+bool flash_supported(const GroupedArgs& a) {
+  return mfma_types_ok(a) && a.L > 128 &&
+         (static_cast<int64_t>(a.L) + FBN) * a.row_stride * a.D * 2 < (int64_t{1} << 31);
+}
 
 hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
   if (!flash_supported(a)) return hipErrorInvalidValue;

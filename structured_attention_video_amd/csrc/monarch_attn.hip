@@ -4,6 +4,7 @@
 #include "../../include/monarch_attn.h"
 
 #include <math.h>
+#include <string.h>
 #include <new>
 
 #include "internal.h"
@@ -83,6 +84,14 @@ hipError_t launch(int32_t kernel, const GroupedArgs& a, hipStream_t s) {
   }
 }
 
+// bit-level test, independent of floating-point compile flags
+bool finite_nonnegative(float x) {
+  uint32_t u;
+  memcpy(&u, &x, sizeof u);
+  if ((u & 0x7f800000u) == 0x7f800000u) return false;  // inf or nan
+  return (u >> 31) == 0 || (u & 0x7fffffffu) == 0;      // +x, or -0
+}
+
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -104,7 +113,7 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
   if (dtype != MONARCH_BF16 && dtype != MONARCH_FP32) return MONARCH_ERR_INVALID_ARG;
   if (align < MONARCH_ALIGN_FRAME || align > MONARCH_ALIGN_CUSTOM) return MONARCH_ERR_INVALID_ARG;
   if (flags & ~kKnownFlags) return MONARCH_ERR_INVALID_ARG;
-  if (!isfinite(scale) || scale < 0.f) return MONARCH_ERR_INVALID_ARG;
+  if (!finite_nonnegative(scale)) return MONARCH_ERR_INVALID_ARG;
   if (tile_tokens < 0) return MONARCH_ERR_INVALID_ARG;
   if (head_dim != 64 && head_dim != 128) return MONARCH_ERR_UNSUPPORTED;
 
