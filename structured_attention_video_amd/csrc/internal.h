@@ -42,7 +42,7 @@ enum KernelId : int32_t {
   kKernelGeneric = 1,   // plain VALU, fp32 arithmetic, any L
   kKernelFlash = 2,     // bf16 MFMA, LDS-staged K/V tiles, online softmax, large L
   kKernelSmall = 3,     // bf16 MFMA, one wavefront per problem, L <= 32
-  kKernelTiny = 4,      // VALU, one problem per thread group, L <= 8
+  kKernelTiny = 4,      // VALU, D/8 lanes per problem, L <= 8, any element types
 };
 
 const char* kernel_name(int32_t id);
@@ -53,5 +53,7 @@ bool flash_supported(const GroupedArgs& a);
 hipError_t launch_flash(const GroupedArgs& a, hipStream_t stream);
 bool small_supported(const GroupedArgs& a);
 hipError_t launch_small(const GroupedArgs& a, hipStream_t stream);
+bool tiny_supported(const GroupedArgs& a);
+hipError_t launch_tiny(const GroupedArgs& a, hipStream_t stream);
 
 }  // namespace monarch

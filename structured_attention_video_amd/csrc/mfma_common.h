@@ -10,9 +10,15 @@
 // and row sum are in-lane reductions plus one swap between the two lane
 // halves. The probabilities P^T leave the accumulator in exactly the B-operand
 // layout of the second product O^T = V^T P^T, with the key order inside each
-// 16-key step permuted: lane half h, element e holds key
-// 8*(e/4) + 4*h + e%4. V^T is stored in LDS with the same permutation of its
-// key slots, so both operands agree and no register shuffle is needed.
+// 16-key step permuted: lane half h, element e holds key 8*(e/4) + 4*h + e%4.
+// V stays row-major in LDS, like K; the V^T A operand is gathered with two
+// transposing reads (ds_read_b64_tr_b16) whose source rows follow the same
+// key permutation, so both operands agree and no register shuffle is needed.
+//
+// ds_read_b64_tr_b16 lane map (measured on gfx950): inside each group of 16
+// lanes, lane i receives element i%4 of the 8-byte segment addressed by lane
+// 4*e + i/4, for e = 0..3. If lane j of the group addresses row key0 + j/4 at
+// channels c0 + 4*(j%4), lane i receives channel c0 + i of rows key0..key0+3.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <math.h>
@@ -25,9 +31,13 @@ namespace mfma {
 
 typedef __bf16 bf16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -45,58 +55,51 @@ __device__ __forceinline__ float halves_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// key (0..n-1 inside a tile) -> V^T slot: inside every 16 keys the groups of
-// four keys 4..7 and 8..11 trade places (an involution)
-__device__ __forceinline__ int key_slot(int k) {
-  const int g = (k >> 2) & 3;
-  const int sg = g == 1 ? 2 : (g == 2 ? 1 : g);
-  return (k & ~15) | (sg << 2) | (k & 3);
-}
-
 // key index of accumulator register i for lane half h, in a 32-key tile
 __device__ __forceinline__ int acc_key(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// LDS geometry: K rows (d contiguous) and V^T rows (keys contiguous), each
-// padded by 16 bytes so that 16 consecutive rows start in distinct banks.
+// LDS rows of K and V (channels contiguous) padded by 32 bytes: the 8 rows of
+// one 16-byte read phase, and the 4 rows x 4 segments of a transposing read,
+// start in distinct banks.
 template <int D>
-struct KRow { static constexpr int bytes = D * 2 + 16; };
-template <int BN>
-struct VRow { static constexpr int bytes = BN * 2 + 16; };
-
-// Interleave two packed bf16 pairs: low halves (sel 0x05040100) or high halves
-// (sel 0x07060302) of lo and hi into one dword [lo.x, hi.x].
-__device__ __forceinline__ uint32_t pack_lo(uint32_t lo, uint32_t hi) {
-  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t lo, uint32_t hi) {
-  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
-}
-
-// Write four keys x eight channels (four 16-byte rows r0..r3 = keys k..k+3,
-// channels d0..d0+7) into V^T: eight 8-byte writes, one per channel.
-template <int BN>
-__device__ __forceinline__ void store_vt4(char* vt, int d0, int slot, const u32x4& r0, const u32x4& r1,
-                                          const u32x4& r2, const u32x4& r3) {
-  constexpr int VR = VRow<BN>::bytes;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a0 = r0[w], a1 = r1[w], a2 = r2[w], a3 = r3[w];
-    u32x2 lo, hi;
-    lo[0] = pack_lo(a0, a1);
-    lo[1] = pack_lo(a2, a3);
-    hi[0] = pack_hi(a0, a1);
-    hi[1] = pack_hi(a2, a3);
-    *reinterpret_cast<u32x2*>(vt + (d0 + 2 * w) * VR + slot * 2) = lo;
-    *reinterpret_cast<u32x2*>(vt + (d0 + 2 * w + 1) * VR + slot * 2) = hi;
-  }
-}
-
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+struct KRow { static constexpr int bytes = D * 2 + 32; };
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// ---------------------------------------------------------------- global access
+// Buffer descriptor over one problem's rows: base = its first token, size =
+// up to the end of its last row. Rows past the end read as zero and stores
+// to them are dropped, so tails need no clamp or branch. The fields are
+// wave-uniform; readfirstlane tells the compiler so (otherwise it keeps them
+// in vector registers and serialises every access).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t problem_rsrc(const void* head, int64_t base_token, int64_t rs,
+                                                               int L, int D, int esize) {
+  const uint64_t addr = reinterpret_cast<uint64_t>(static_cast<const char*>(head) + base_token * D * esize);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(addr >> 32));
+  const uint32_t bytes =
+      __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(((static_cast<int64_t>(L) - 1) * rs + 1) * D * esize));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, static_cast<short>(0), static_cast<int>(bytes), 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(off), 0, 0));
+}
+
+// One 32-row query fragment as MFMA B operands: lane l reads row l%32,
+// channels 16*ks + 8*(l/32) .. +8 (rows past the end read as zero).
+template <int D>
+__device__ __forceinline__ void load_qfrag(bf16x8 (&qf)[D / 16], __amdgpu_buffer_rsrc_t rq, int row0, int64_t rs,
+                                           int lane) {
+  const uint32_t off = static_cast<uint32_t>(((row0 + (lane & 31)) * rs * D + (lane >> 5) * 8) * 2);
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = __builtin_bit_cast(bf16x8, bload16(rq, off + ks * 32));
+}
+
+// ---------------------------------------------------------------- matrix products
 // S^T for one 32-key tile of K in LDS (rows key0..key0+31) against a wave's
-// query fragment qf (B operand, one bf16x8 per 16 channels).
+// query fragment qf.
 template <int D>
 __device__ __forceinline__ f32x16 scores_tile(const char* kl, int key0, const bf16x8 (&qf)[D / 16], int lane) {
   constexpr int KR = KRow<D>::bytes;
@@ -107,12 +110,26 @@ __device__ __forceinline__ f32x16 scores_tile(const char* kl, int key0, const bf
   return s;
 }
 
-// O^T[32*mt .. +32) += V^T P^T over one 16-key step (slots 16*step ..)
-template <int BN>
-__device__ __forceinline__ f32x16 pv_step(const char* vt, int mt, int step, bf16x8 p, f32x16 o, int lane) {
-  constexpr int VR = VRow<BN>::bytes;
-  const char* row = vt + (32 * mt + (lane & 31)) * VR + step * 32 + (lane >> 5) * 16;
-  return mma(ld_bf16x8(row), p, o);
+// V^T A operand for channels 32*mt .. +32 and the 16-key step `step` of a
+// row-major V tile in LDS: lane half h element e holds key
+// 16*step + 8*(e/4) + 4*h + e%4 (two transposing reads, keys +0..3 / +8..11).
+template <int D>
+__device__ __forceinline__ bf16x8 vt_operand(const char* vl, int mt, int step, int lane) {
+  constexpr int R = KRow<D>::bytes;
+  const int j = lane & 15, g = lane >> 4;
+  const int key = 16 * step + 4 * (g >> 1) + (j >> 2);
+  const int ch = 32 * mt + 16 * (g & 1) + 4 * (j & 3);
+  const char* p = vl + key * R + ch * 2;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * R));
+  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// O^T[32*mt .. +32) += V^T P^T over one 16-key step
+template <int D>
+__device__ __forceinline__ f32x16 pv_step(const char* vl, int mt, int step, bf16x8 p, f32x16 o, int lane) {
+  return mma(vt_operand<D>(vl, mt, step, lane), p, o);
 }
 
 // bf16 B operand for PV step `step` from probabilities held as accumulator
@@ -124,27 +141,30 @@ __device__ __forceinline__ bf16x8 p_operand(const f32x16& p, int half) {
   return r;
 }
 
-// Write one lane's share of O (query row `row`, all D channels) from O^T
-// accumulators; channel of register i in tile mt is 32*mt + acc_key(i, h).
+// Write one lane's share of O (query row `row` of the problem, all D
+// channels) from O^T accumulators through the problem's descriptor (rows past
+// the end are dropped). Channel of register i in tile mt is 32*mt + acc_key(i, h).
 template <int D, bool OUT_F32>
-__device__ __forceinline__ void store_out(void* out, int64_t row_elem, const f32x16 (&o)[D / 32], float inv,
-                                          int lane) {
+__device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t ro, int row, int64_t rs, const f32x16 (&o)[D / 32],
+                                          float inv, int lane) {
   const int h = lane >> 5;
+  const uint32_t esz = OUT_F32 ? 4 : 2;
+  const uint32_t rowoff = static_cast<uint32_t>(row * rs * D) * esz;
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const int d = 32 * mt + 8 * g + 4 * h;
+      const uint32_t off = rowoff + (32 * mt + 8 * g + 4 * h) * esz;
       if (OUT_F32) {
-        float4 v = make_float4(o[mt][4 * g] * inv, o[mt][4 * g + 1] * inv, o[mt][4 * g + 2] * inv,
-                               o[mt][4 * g + 3] * inv);
-        *reinterpret_cast<float4*>(static_cast<float*>(out) + row_elem + d) = v;
+        u32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(o[mt][4 * g + e] * inv);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(off), 0, 0);
       } else {
-        typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(o[mt][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(out) + row_elem + d) = v;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, static_cast<int>(off), 0, 0);
       }
     }
   }

@@ -70,6 +70,7 @@ GroupedArgs stage2_args(const monarch_plan_info& p, const void* q, const void* k
 
 int32_t choose_kernel(const GroupedArgs& a, uint32_t flags) {
   if (!(flags & MONARCH_FLAG_GENERIC)) {
+    if (tiny_supported(a)) return kKernelTiny;
     if (small_supported(a)) return kKernelSmall;
     if (flash_supported(a)) return kKernelFlash;
   }
@@ -80,6 +81,7 @@ hipError_t launch(int32_t kernel, const GroupedArgs& a, hipStream_t s) {
   switch (kernel) {
     case kKernelFlash: return launch_flash(a, s);
     case kKernelSmall: return launch_small(a, s);
+    case kKernelTiny: return launch_tiny(a, s);
     default: return launch_generic(a, s);
   }
 }

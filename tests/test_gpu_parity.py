@@ -220,3 +220,29 @@ def test_inblock_permutation_equivariance_full_size():
     o = run(q, k, v, c["grid"], "frame")
     op = run(q[:, :, perm], k[:, :, perm], v[:, :, perm], c["grid"], "frame")
     assert_close(to_np(op), to_np(o[:, :, perm]), BF16, "permuted blocks")
+
+
+def test_stage1_full_size_all_heads():
+    # the first factor alone, every head of the frame workload (stage 2 would
+    # average errors over 21 blocks and hide a wrong row)
+    q, k, v = datagen.config_inputs("frame_bf16")
+    plan = MonarchPlan(1, 12, 128, (21, 30, 52), align="frame")
+    y = plan.stage1(q.to(DEV), k.to(DEV), v.to(DEV))
+    torch.cuda.synchronize()
+    Y = to_np(y)[0]
+    for h in range(12):
+        yref = oracle.stage1(to_np(q[0, h]), to_np(k[0, h]), to_np(v[0, h]), 1560, 128 ** -0.5)
+        assert_close(Y[h], yref, BF16, f"stage 1 head {h}")
+
+
+@pytest.mark.parametrize("name", ["frame_bf16", "tiled_bf16", "row_bf16"])
+def test_forward_is_deterministic(name):
+    c = datagen.CONFIGS[name]
+    q, k, v = (x.to(DEV) for x in datagen.config_inputs(name))
+    plan = MonarchPlan(1, 12, 128, c["grid"], align=c["align"], tile_tokens=c["tile_tokens"])
+    outs = [plan.forward(q, k, v) for _ in range(3)]
+    y = plan.stage1(q, k, v)
+    o2 = plan.stage2(q, k, y)
+    torch.cuda.synchronize()
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    assert torch.equal(outs[0], o2)
