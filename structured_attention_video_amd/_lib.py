@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmonarch_attn.so")
+# MONARCH_ATTN_LIB may point at another build of the same library (e.g. a
+# tuning variant); by default the in-tree build is loaded.
+LIB_PATH = os.environ.get("MONARCH_ATTN_LIB") or os.path.join(_HERE, "libmonarch_attn.so")
 
 # status codes (monarch_status)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_UNALIGNED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(7)

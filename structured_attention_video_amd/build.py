@@ -43,9 +43,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, obj: str) -> None:
+def _compile(src: str, obj: str, dflags=()) -> None:
     extra = KERNEL_FLAGS if os.path.basename(src).startswith("kernel_") else []
-    cmd = [hipcc(), *FLAGS, *extra, "-c", src, "-o", obj]
+    cmd = [hipcc(), *FLAGS, *extra, *dflags, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(x for x in r.stderr.splitlines() if "packed-fp32-ops" not in x)
     if r.returncode != 0:
@@ -54,25 +54,29 @@ def _compile(src: str, obj: str) -> None:
         sys.stderr.write(err + "\n")
 
 
-def build(jobs: int = 8, verbose: bool = True) -> str:
-    bdir = os.path.join(CSRC, "_build")
+def build(jobs: int = 8, verbose: bool = True, out: str = OUT, defines=()) -> str:
+    bdir = os.path.join(CSRC, "_build" + ("_" + "_".join(d.replace("=", "") for d in defines) if defines else ""))
     os.makedirs(bdir, exist_ok=True)
     srcs = sources()
     objs = [os.path.join(bdir, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    dflags = [f"-D{d}" for d in defines]
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        list(ex.map(_compile, srcs, objs))
-    tmp = OUT + ".tmp"
+        list(ex.map(lambda s_o: _compile(*s_o, dflags), zip(srcs, objs)))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
     if verbose:
-        print(f"built {OUT}")
-    return OUT
+        print(f"built {out}")
+    return out
 
 
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=min(8, os.cpu_count() or 1))
-    build(ap.parse_args().jobs)
+    ap.add_argument("--out", default=OUT, help="output library path")
+    ap.add_argument("-D", dest="defines", action="append", default=[], help="extra preprocessor define")
+    a = ap.parse_args()
+    build(a.jobs, out=a.out, defines=a.defines)

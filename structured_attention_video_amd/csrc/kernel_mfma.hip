@@ -72,26 +72,80 @@ constexpr int FBM = 128;  // query rows per workgroup
 constexpr int FBN = 64;   // keys per LDS tile
 constexpr int FNT = 256;  // threads
 
+// LDS tiles of the flash kernel: 64 rows x D channels, rows unpadded, the
+// 16-byte chunks of row r permuted by c -> c ^ swz(r). Tiles are filled by
+// buffer loads that write LDS directly (64 lanes x 16 bytes = one contiguous
+// kilobyte per instruction; lane i fetches the global chunk that belongs in
+// slot i). The swizzle keeps every 16-lane phase of the 16-byte K reads and
+// of the transposing V reads on distinct banks.
 template <int D>
-struct FlashLds {
-  static constexpr int tile = FBN * KRow<D>::bytes;  // one K or V tile
-  static constexpr int total = 4 * tile;             // two-slot rings for K and V
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) return ((2 * r) & 15) | ((r >> 3) & 1);
+  else return (2 * ((r >> 1) & 3)) | ((r >> 3) & 1);
+}
+
+template <int D>
+struct SwTile {
+  static constexpr int ROWB = D * 2;          // bytes per row
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int bytes = FBN * ROWB;    // one tile
+  static constexpr int RPI = 1024 / ROWB;     // rows per load instruction
+  static constexpr int IPW = FBN / 4 / RPI;   // load instructions per wave per tile
+  static constexpr int total = 4 * bytes;     // two-slot rings for K and V
 };
 
-// S^T for a 64-key tile: two independent 32-key accumulator chains
-template <int D>
-__device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const bf16x8 (&qf)[D / 16], int lane) {
-  constexpr int KR = KRow<D>::bytes;
-  const char* r0 = kl + (lane & 31) * KR + (lane >> 5) * 16;
-  const char* r1 = r0 + 32 * KR;
-  s[0] = f32x16{};
-  s[1] = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    s[0] = mma(ld_bf16x8(r0 + ks * 32), qf[ks], s[0]);
-    s[1] = mma(ld_bf16x8(r1 + ks * 32), qf[ks], s[1]);
-  }
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from a buffer straight into LDS (lane i -> lds + 16*i).
+// Only the device pass sees the builtin: instantiating it in the host pass
+// silently drops the host launch stub of the kernel that uses it, and device
+// functions never run on the host.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t src, char* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds, 16, voff, 0, 0, 0);
+#else
+  (void)src; (void)lds; (void)voff;
+#endif
 }
+
+
+// Per-lane byte offsets: DMA source chunks (tile 0) and LDS read addresses.
+template <int D>
+struct FlashOffsets {
+  using T = SwTile<D>;
+  uint32_t src_off[T::IPW];  // global, relative to the tile's first row
+  uint32_t k[D / 16];     // K read, k-step ks, rows 0..31 (+32 rows = +32*ROWB)
+  uint32_t v[D / 32][2];  // V^T reads, channel tile mt, keys +0..3 / +8..11 (+16*step rows)
+  __device__ __forceinline__ FlashOffsets(int wave, int lane, int64_t rs) {
+#pragma unroll
+    for (int i = 0; i < T::IPW; ++i) {
+      const int row = 16 * wave + T::RPI * i + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ swz<D>(row);
+      src_off[i] = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
+    }
+    const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k[ks] = r * T::ROWB + 16 * ((2 * ks + h) ^ swz<D>(r));
+    const int j = lane & 15, g = lane >> 4;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int sec = 0; sec < 2; ++sec) {
+        const int row = 4 * (g >> 1) + (j >> 2) + 8 * sec;
+        const int ch = 32 * mt + 16 * (g & 1) + 4 * (j & 3);
+        v[mt][sec] = row * T::ROWB + 16 * ((ch / 8) ^ swz<D>(row)) + (ch % 8) * 2;
+      }
+  }
+  // Issue this wave's share (16 rows) of one tile's global -> LDS copy.
+  __device__ __forceinline__ void dma(char* tile, __amdgpu_buffer_rsrc_t src, uint32_t tile_off, int wave) const {
+#pragma unroll
+    for (int i = 0; i < T::IPW; ++i)
+      lds_dma16(src, tile + (16 * wave + T::RPI * i) * T::ROWB, src_off[i] + tile_off);
+  }
+};
+
+// wait for this wave's outstanding global -> LDS copies
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int nvalid, int h) {
 #pragma unroll
@@ -118,8 +172,72 @@ __device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D /
   }
 }
 
-// exp2(s*c - m) as bf16 B operands for the four 16-key PV steps; adds the
-// unnormalised weights to l.
+template <int D>
+__device__ __forceinline__ bf16x8 k_operand(const char* kl, const FlashOffsets<D>& fo, int ks, int t) {
+  return ld_bf16x8(kl + fo.k[ks] + t * 32 * SwTile<D>::ROWB);
+}
+
+template <int D>
+__device__ __forceinline__ bf16x8 v_operand(const char* vl, const FlashOffsets<D>& fo, int mt, int st) {
+  const char* base = vl + st * 16 * SwTile<D>::ROWB;
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + fo.v[mt][0]));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + fo.v[mt][1]));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// S^T for a 64-key tile (two independent 32-key accumulator chains)
+template <int D>
+__device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const FlashOffsets<D>& fo,
+                                         const bf16x8 (&qf)[D / 16]) {
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    s[0] = mma(k_operand<D>(kl, fo, ks, 0), qf[ks], s[0]);
+    s[1] = mma(k_operand<D>(kl, fo, ks, 1), qf[ks], s[1]);
+  }
+}
+
+// Scores of the next tile interleaved with the probabilities of the current
+// one: each 16-channel step (two MFMAs, K read one step ahead) carries a
+// slice of the exponentials; sched_barrier keeps the steps apart so the
+// compiler does not regroup all MFMAs first.
+template <int D>
+__device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* kl, const FlashOffsets<D>& fo,
+                                                  const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
+                                                  bf16x8 (&pb)[4], float& l, float c, float m) {
+  constexpr int KS = D / 16;
+  constexpr int PER = 32 / KS;
+  sn[0] = f32x16{};
+  sn[1] = f32x16{};
+  float p[32];
+  bf16x8 a0 = k_operand<D>(kl, fo, 0, 0), a1 = k_operand<D>(kl, fo, 0, 1);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 n0 = a0, n1 = a1;
+    if (ks + 1 < KS) {
+      n0 = k_operand<D>(kl, fo, ks + 1, 0);
+      n1 = k_operand<D>(kl, fo, ks + 1, 1);
+    }
+    sn[0] = mma(a0, qf[ks], sn[0]);
+    sn[1] = mma(a1, qf[ks], sn[1]);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int i = ks * PER + e;
+      p[i] = fast_exp2(fmaf(s[i >> 4][i & 15], c, -m));
+      l += p[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    a0 = n0;
+    a1 = n1;
+  }
+#pragma unroll
+  for (int st = 0; st < 4; ++st)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pb[st][e] = static_cast<bf16>(p[8 * st + e]);
+}
+
+// exp2(s*c - m) as bf16 B operands for the four 16-key PV steps (last tile)
 __device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float c, float m) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
@@ -132,24 +250,48 @@ __device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], flo
   }
 }
 
+// O^T += V^T P^T over `steps` 16-key steps, next step's V^T read one step ahead
 template <int D>
-__device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vl, const bf16x8 (&pb)[4], int steps, int lane) {
+__device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vl, const FlashOffsets<D>& fo,
+                                     const bf16x8 (&pb)[4], int steps) {
+  constexpr int MT = D / 32;
+  bf16x8 v[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) v[mt] = v_operand<D>(vl, fo, mt, 0);
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     if (st < steps) {
+      bf16x8 nv[MT];
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) o[mt] = pv_step<D>(vl, mt, st, pb[st], o[mt], lane);
+      for (int mt = 0; mt < MT; ++mt) nv[mt] = (st + 1 < 4) ? v_operand<D>(vl, fo, mt, st + 1) : v[mt];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) o[mt] = mma(v[mt], pb[st], o[mt]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) v[mt] = nv[mt];
     }
   }
 }
 
+// Mutable per-wave state of the flash loop.
+template <int D>
+struct FlashState {
+  f32x16 s[2];       // scores of the current tile (raw)
+  f32x16 o[D / 32];  // O^T accumulators
+  float m, l;        // running max (scaled) and partial sum
+
+};
+
 template <int D, bool OUT_F32>
 __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles, int nwg) {
-  using FL = FlashLds<D>;
-  using TO = TileOffsets<D, FBN, FNT>;
-  __shared__ __attribute__((aligned(16))) char smem[FL::total];
-  char* const kring = smem;
-  char* const vring = smem + 2 * FL::tile;
+  using T = SwTile<D>;
+  // four separate arrays (not fields of one): the compiler then proves that
+  // reads of one slot never alias the asynchronous copy into another and
+  // waits for the copies only at the barrier
+  __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
 
   const int id = xcd_order(blockIdx.x, nwg);
   const int qt = id % qtiles;
@@ -173,62 +315,67 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
   const int n = (L + FBN - 1) / FBN;
   const int nv_last = L - (n - 1) * FBN;
   const float c = a.scale_log2;
-  const TO to(tid, rs);
+  const FlashOffsets<D> fo(wave, lane, rs);
   const uint32_t tile_bytes = static_cast<uint32_t>(FBN * rs * D * 2);
 
+  // prologue: K tiles 0 and 1, V tile 0
+  fo.dma(k0, rk, 0, wave);
+  fo.dma(v0, rv, 0, wave);
+  if (n > 1) fo.dma(k1, rk, tile_bytes, wave);
   bf16x8 qf[D / 16];
   load_qfrag<D>(qf, rq, row0, rs, lane);
-  f32x16 o[D / 32];
+  FlashState<D> st;
 #pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
-  float m = -INFINITY, l = 0.f;
-
-  u32x4 gk[TO::N], gv[TO::N];
-  to.load(gk, rk, 0);
-  to.load(gv, rv, 0);
-  to.store(kring, gk);
-  to.store(vring, gv);
-  if (n > 1) {
-    to.load(gk, rk, tile_bytes);
-    to.store(kring + FL::tile, gk);
-  }
+  for (int mt = 0; mt < D / 32; ++mt) st.o[mt] = f32x16{};
+  st.m = -INFINITY;
+  st.l = 0.f;
+  wait_dma();
   __syncthreads();
 
-  f32x16 s[2];
-  if (active) scores64<D>(s, kring, qf, lane);
-  // iteration 0 overwrites K ring slot 0 (tile 0) with tile 2: every wave
-  // must be done reading it
+  if (active) scores64<D>(st.s, k0, fo, qf);
+  // iteration 0 refills K slot 0 (tile 0): every wave must be done with it
   __syncthreads();
 
-  // steady state: every iteration has a next tile
-  for (int j = 0; j + 1 < n; ++j) {
-    if (j + 2 < n) to.load(gk, rk, (j + 2) * tile_bytes);
-    to.load(gv, rv, (j + 1) * tile_bytes);
+  // Iteration j: copy K_{j+2} into kdma and V_{j+1} into vdma (global ->
+  // LDS, asynchronous), then the scores of tile j+1 from kread while the
+  // softmax of tile j runs, then its value product from vread. The four LDS
+  // slots are distinct fields so the compiler can see that the reads never
+  // touch the tiles being copied and does not wait for the copies first.
+  auto step = [&](int j, char* kdma, char* vdma, const char* kread, const char* vread) {
+    if (j + 2 < n) fo.dma(kdma, rk, (j + 2) * tile_bytes, wave);
+    fo.dma(vdma, rv, (j + 1) * tile_bytes, wave);
     if (active) {
-      update_max<D>(s, o, m, l, c);
+      update_max<D>(st.s, st.o, st.m, st.l, c);
       f32x16 sn[2];
-      scores64<D>(sn, kring + ((j + 1) & 1) * FL::tile, qf, lane);
       bf16x8 pb[4];
-      probs(s, pb, l, c, m);
-      pv64<D>(o, vring + (j & 1) * FL::tile, pb, 4, lane);
-      s[0] = sn[0];
-      s[1] = sn[1];
+      scores_with_probs<D>(sn, kread, fo, qf, st.s, pb, st.l, c, st.m);
+      pv64<D>(st.o, vread, fo, pb, 4);
+      st.s[0] = sn[0];
+      st.s[1] = sn[1];
     }
-    if (j + 2 < n) to.store(kring + (j & 1) * FL::tile, gk);
-    to.store(vring + ((j + 1) & 1) * FL::tile, gv);
+    wait_dma();
     __syncthreads();
+  };
+
+  // steady state, two iterations per trip so every slot is a fixed array:
+  // even j copies into (k0, v1) and reads (k1, v0); odd j the reverse
+  int j = 0;
+  for (; j + 2 < n; j += 2) {
+    step(j, k0, v1, k1, v0);
+    step(j + 1, k1, v0, k0, v1);
   }
+  if (j + 1 < n) step(j, k0, v1, k1, v0);
 
   if (!active) return;
   // last tile: mask keys past the end, skip the empty half of the PV product
-  if (nv_last < FBN) mask_tail(s, nv_last, h);
-  update_max<D>(s, o, m, l, c);
+  if (nv_last < FBN) mask_tail(st.s, nv_last, h);
+  update_max<D>(st.s, st.o, st.m, st.l, c);
   bf16x8 pb[4];
-  probs(s, pb, l, c, m);
-  pv64<D>(o, vring + ((n - 1) & 1) * FL::tile, pb, nv_last > 32 ? 4 : 2, lane);
+  probs(st.s, pb, st.l, c, st.m);
+  pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
-  const float inv = 1.f / halves_sum(l);  // both lane halves of a row are active together
-  store_out<D, OUT_F32>(ro, row0 + (lane & 31), rs, o, inv, lane);
+  const float inv = 1.f / halves_sum(st.l);  // both lane halves of a row are active together
+  store_out<D, OUT_F32>(ro, row0 + (lane & 31), rs, st.o, inv, lane);
 }
 
 // ---------------------------------------------------------------- group

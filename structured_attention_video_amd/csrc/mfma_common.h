@@ -58,11 +58,16 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // key index of accumulator register i for lane half h, in a 32-key tile
 __device__ __forceinline__ int acc_key(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// LDS rows of K and V (channels contiguous) padded by 32 bytes: the 8 rows of
-// one 16-byte read phase, and the 4 rows x 4 segments of a transposing read,
-// start in distinct banks.
+// LDS rows of K and V (channels contiguous) are padded by 32 bytes: the 8
+// rows of a 16-byte read phase, and the 4 rows x 4 segments of a transposing
+// read, start in distinct banks. (48 bytes also clears the 16-row phase and
+// halves the measured conflict cycles, but measured slower: 77.8 KB of LDS
+// per workgroup leaves almost none spare with two workgroups per CU.)
+#ifndef MONARCH_ROW_PAD
+#define MONARCH_ROW_PAD 32
+#endif
 template <int D>
-struct KRow { static constexpr int bytes = D * 2 + 32; };
+struct KRow { static constexpr int bytes = D * 2 + MONARCH_ROW_PAD; };
 
 __device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 

@@ -1,7 +1,7 @@
 // C-ABI layer: plan validation, workspace sizing, pointer checks and kernel
 // dispatch for the two Monarch stages. Everything before a launch is plain
 // host arithmetic, so every error path runs without a GPU.
-#include "../../include/monarch_attn.h"
+#include "monarch_attn.h"
 
 #include <math.h>
 #include <string.h>
