@@ -273,6 +273,14 @@ __device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vl, const 
   }
 }
 
+// Wave priority while issuing MFMA-heavy phases (MONARCH_PRIO): 0 = never
+// raised; 1 = raised for the value product; 2 = raised for scores + values
+// (measured best: the two waves sharing a SIMD then tend to alternate
+// between their MFMA and softmax phases instead of colliding).
+#ifndef MONARCH_PRIO
+#define MONARCH_PRIO 2
+#endif
+
 // Mutable per-wave state of the flash loop.
 template <int D>
 struct FlashState {
@@ -348,8 +356,17 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
       update_max<D>(st.s, st.o, st.m, st.l, c);
       f32x16 sn[2];
       bf16x8 pb[4];
+#if MONARCH_PRIO == 2
+      __builtin_amdgcn_s_setprio(1);
+#endif
       scores_with_probs<D>(sn, kread, fo, qf, st.s, pb, st.l, c, st.m);
+#if MONARCH_PRIO == 1
+      __builtin_amdgcn_s_setprio(1);
+#endif
       pv64<D>(st.o, vread, fo, pb, 4);
+#if MONARCH_PRIO
+      __builtin_amdgcn_s_setprio(0);
+#endif
       st.s[0] = sn[0];
       st.s[1] = sn[1];
     }
@@ -379,20 +396,35 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
 }
 
 // ---------------------------------------------------------------- group
+// One problem (at most 128 rows) per workgroup, one wave per 32 query rows.
+// Q, K and V rows are copied global -> LDS whole (each DMA instruction moves
+// four 256-byte rows), scores and values run from LDS, and O goes back
+// through LDS so that it leaves as whole 256-byte rows too. Every global
+// access is a full-row, coalesced 16-byte-per-lane access: for stage-2
+// groups (rows a block apart) this is what keeps the L2 request count down.
 template <int D, int QT>
 struct GroupCfg {
-  static constexpr int BN = 32 * QT;  // keys (padded to whole 32-key tiles)
-  static constexpr int NT = 64 * QT;  // one wave per 32 query rows
-  static constexpr int lds = 2 * BN * KRow<D>::bytes;
+  static constexpr int BN = 32 * QT;       // rows per tile (keys = queries)
+  static constexpr int NT = 64 * QT;       // one wave per 32 query rows
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;        // 16-byte chunks per row
+  static constexpr int tile = BN * ROWB;
+  static constexpr int RPI = 1024 / ROWB;  // rows per DMA instruction
+  static constexpr int IPW = 32 / RPI;     // DMA instructions per wave per tile
 };
+
+// byte offset of 16-byte chunk c of row r in a swizzled tile
+template <int D>
+__device__ __forceinline__ int swoff(int r, int c) {
+  return r * D * 2 + 16 * (c ^ swz<D>(r));
+}
 
 template <int D, int QT, bool OUT_F32>
 __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(GroupedArgs a) {
   using G = GroupCfg<D, QT>;
-  using TO = TileOffsets<D, G::BN, G::NT>;
-  __shared__ __attribute__((aligned(16))) char smem[G::lds];
-  char* const kl = smem;
-  char* const vl = smem + G::BN * KRow<D>::bytes;
+  __shared__ __attribute__((aligned(1024))) char ql[G::tile];
+  __shared__ __attribute__((aligned(1024))) char kl[G::tile];
+  __shared__ __attribute__((aligned(1024))) char vl[G::tile];
 
   const int p = blockIdx.x % a.problems;
   const int hd = blockIdx.x / a.problems;
@@ -406,24 +438,35 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(Grouped
   const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), base, rs, L, D,
                                OUT_F32 ? 4 : 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int row0 = wave * 32;
 
-  bf16x8 qf[D / 16];
-  load_qfrag<D>(qf, rq, row0, rs, lane);
-  const TO to(tid, rs);
-  {
-    u32x4 gk[TO::N], gv[TO::N];
-    to.load(gk, rk, 0);
-    to.load(gv, rv, 0);
-    to.store(kl, gk);
-    to.store(vl, gv);
+  // wave w copies rows 32w .. 32w+31 of Q, K and V (rows past L read as zero)
+#pragma unroll
+  for (int i = 0; i < G::IPW; ++i) {
+    const int row = 32 * wave + G::RPI * i + lane / G::CPR;
+    const int c = (lane % G::CPR) ^ swz<D>(row);
+    const uint32_t goff = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
+    const int dst = (32 * wave + G::RPI * i) * G::ROWB;
+    lds_dma16(rq, ql + dst, goff);
+    lds_dma16(rk, kl + dst, goff);
+    lds_dma16(rv, vl + dst, goff);
   }
+  wait_dma();
   __syncthreads();
+
+  const int r = 32 * wave + (lane & 31);  // this lane's query row
+  bf16x8 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld_bf16x8(ql + swoff<D>(r, 2 * ks + h));
 
   const float c = a.scale_log2;
   f32x16 s[QT];
 #pragma unroll
-  for (int t = 0; t < QT; ++t) s[t] = scores_tile<D>(kl, 32 * t, qf, lane);
+  for (int t = 0; t < QT; ++t) {
+    s[t] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      s[t] = mma(ld_bf16x8(kl + swoff<D>(32 * t + (lane & 31), 2 * ks + h)), qf[ks], s[t]);
+  }
   float mx = -INFINITY;
 #pragma unroll
   for (int t = 0; t < QT; ++t)
@@ -444,14 +487,46 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(Grouped
   f32x16 o[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
+  const int j = lane & 15, g = lane >> 4;
 #pragma unroll
   for (int st = 0; st < 2 * QT; ++st) {
     const bf16x8 pb = p_operand(s[st >> 1], st & 1);
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) o[mt] = pv_step<D>(vl, mt, st, pb, o[mt], lane);
+    for (int mt = 0; mt < D / 32; ++mt) {
+      // V^T operand: keys 16*st + 4*(g/2) + j/4 (+8), channels 32*mt + 16*(g%2) + 4*(j%4) + 0..3
+      const int row = 16 * st + 4 * (g >> 1) + (j >> 2);
+      const int ch = 32 * mt + 16 * (g & 1) + 4 * (j & 3);
+      const char* p0 = vl + swoff<D>(row, ch / 8) + (ch % 8) * 2;
+      const char* p1 = vl + swoff<D>(row + 8, ch / 8) + (ch % 8) * 2;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p0);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p1);
+      o[mt] = mma(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), pb, o[mt]);
+    }
   }
   const float inv = 1.f / halves_sum(l);
-  store_out<D, OUT_F32>(ro, row0 + (lane & 31), rs, o, inv, lane);
+  if constexpr (OUT_F32) {
+    store_out<D, true>(ro, r, rs, o, inv, lane);
+  } else {
+    // stage O in this wave's own Q rows (row-major, swizzled), then write
+    // whole rows: 16 lanes x 16 bytes per 256-byte row
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(o[mt][4 * gg + e] * inv);
+        *reinterpret_cast<bf16x4*>(ql + swoff<D>(r, 4 * mt + gg) + 8 * h) = v;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32 * G::CPR / 64; ++i) {
+      const int idx = 64 * i + lane;
+      const int row = 32 * wave + idx / G::CPR, chk = idx % G::CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ql + swoff<D>(row, chk));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>((row * rs * D + chk * 8) * 2), 0, 0);
+    }
+  }
 }
 
 bool mfma_types_ok(const GroupedArgs& a) {
