@@ -10,10 +10,15 @@ Prints ONE JSON line. Besides the contract fields it carries:
   roofline      the dominant kernel's achieved rate against its roofline,
                 timed with HIP events on the stream the kernels run on;
   cpu_baseline  the fp64 oracle timed on a bounded sample on the host cores;
-  stages        per-stage ms and rates; dense: the library's own dense
-                softmax-attention kernel at the same shape.
+  stages_two_launch  per-stage ms and rates of the two-launch path (stage 1
+                then stage 2), timed separately; dense: the library's own
+                dense softmax-attention kernel at the same shape.
+A call is stage 1 then stage 2 (two launches); --fused auto/on times the
+library's one-launch fused variant instead where it applies (frame and tiled
+alignments). call_ms_events: per-call device time from HIP events in a second
+loop (the timed loop itself has nothing between the calls).
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config frame_bf16]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 30] [--config frame_bf16]
 """
 from __future__ import annotations
 
@@ -37,13 +42,16 @@ RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="frame_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--fused", choices=["auto", "on", "off"], default="off",
+                    help="one fused launch for both stages: where it applies (auto), required (on), "
+                         "never (off, the default: the two-launch path measures faster)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
     return ap.parse_args()
@@ -145,66 +153,90 @@ def main():
     q_cpu, k_cpu, v_cpu = datagen.config_inputs(args.config)
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (q_cpu, k_cpu, v_cpu))
-    plan = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align=c["align"],
-                       tile_tokens=c["tile_tokens"], dtype=dt)
+    mk = lambda fused: MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align=c["align"],
+                                   tile_tokens=c["tile_tokens"], dtype=dt, fused=fused)
+    plan = mk(args.fused != "off")
+    if args.fused == "on" and not plan.fused:
+        print(json.dumps({"error": f"the fused launch does not apply to {args.config}"}))
+        sys.exit(2)
+    split = mk(False)  # the two-launch path, timed per stage for context
     info = plan.info
-    k1, k2 = plan.kernel_names()
+    k1, k2 = split.kernel_names()
     has1, has2 = info["b"] > 1, info["m_tau"] > 1
     o = torch.empty_like(q)
-    y = torch.empty(q.shape, dtype=plan.y_dtype, device=dev) if (has1 and has2) else None
+    ws = plan.new_workspace(dev)
+    y = torch.empty(q.shape, dtype=split.y_dtype, device=dev) if (has1 and has2) else None
 
-    def step(evs=None):
-        # one forward = stage 1 then stage 2 on the current stream (what
-        # monarch_attn_forward enqueues), with events between the launches
-        if evs is not None:
-            evs[0].record()
-        if has1 and has2:
-            plan.stage1(q, k, v, y)
-            if evs is not None:
-                evs[1].record()
-            plan.stage2(q, k, y, o)
-        else:
-            plan.forward(q, k, v, out=o)
-            if evs is not None:
-                evs[1].record()
-        if evs is not None:
-            evs[2].record()
+    def call():
+        plan.forward(q, k, v, out=o, workspace=ws)
+
+    def timed(fn, n):
+        """n calls of fn with HIP events around each (torch's current stream,
+        where the library launches): per-call device times, sorted."""
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        torch.cuda.synchronize()
+        for i in range(n):
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return sorted(e[0].elapsed_time(e[1]) for e in ev)
 
     for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        call()
+    # the timed region: exactly `steps` calls, nothing else enqueued between them
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
+    for _ in range(args.steps):
+        call()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) / args.steps * 1e3
-    s1 = sorted(e[0].elapsed_time(e[1]) for e in events)
-    s2 = sorted(e[1].elapsed_time(e[2]) for e in events)
-    mean = lambda xs: sum(xs) / len(xs)
-    ms1, ms2 = mean(s1), mean(s2)
+    ms_step = (time.perf_counter() - t0) / args.steps * 1e3
+    per_call = timed(call, args.steps)
+    pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
+
+    # per-stage times of the two-launch path (context, and the roofline when not fused)
+    stage_ms = {}
+    if has1 and has2:
+        for _ in range(2):
+            split.stage1(q, k, v, y)
+            split.stage2(q, k, y, o)
+        t1 = timed(lambda: split.stage1(q, k, v, y), args.steps)
+        t2 = timed(lambda: split.stage2(q, k, y, o), args.steps)
+        stage_ms = {"stage1": sum(t1) / len(t1), "stage2": sum(t2) / len(t2)}
+        call()  # leave o = the measured path's output
+    else:
+        stage_ms = {"stage1" if has1 or not has2 else "stage2": sum(per_call) / len(per_call)}
 
     flops = info["flops_stage1"] + info["flops_stage2"]
     tflops = flops / (ms_step * 1e-3) / 1e12
     esz = 2 if c["dtype"] == "bf16" else 4
     tensor_b = c["batch"] * c["heads"] * info["N"] * c["d"] * esz
-    yb = tensor_b if plan.y_dtype == dt else tensor_b * 2
+    yb = tensor_b if split.y_dtype == dt else tensor_b * 2
     # algorithmic bytes per launch: stage 1 reads Q,K,V writes Y; stage 2 reads Q,K,Y writes O
     bytes1 = 3 * tensor_b + (yb if has2 else 0) if has1 or not has2 else 0
     bytes2 = 2 * tensor_b + (yb if has1 else tensor_b) + tensor_b if has2 else 0
     stages = []
-    if has1 or not has2:
-        stages.append(dict(kernel=k1, launch="stage1", flops=info["flops_stage1"], bytes=bytes1, ms=ms1))
-    if has2:
+    if "stage1" in stage_ms:
+        stages.append(dict(kernel=k1, launch="stage1", flops=info["flops_stage1"] or flops, bytes=bytes1,
+                           ms=stage_ms["stage1"]))
+    if "stage2" in stage_ms:
         stages.append(dict(kernel=k2, launch="stage2", flops=info["flops_stage2"], bytes=bytes2,
-                           ms=ms2 if (has1 and has2) else ms1))
-    for s in stages:
-        s["tflops"] = s["flops"] / (s["ms"] * 1e-3) / 1e12
-        s["gbs"] = s["bytes"] / (s["ms"] * 1e-3) / 1e9
-        s["bound"] = "mfma" if s["flops"] / max(s["bytes"], 1) > RIDGE else "hbm"
-    dom = max(stages, key=lambda s: s["ms"])
+                           ms=stage_ms["stage2"]))
+    for st in stages:
+        st["tflops"] = st["flops"] / (st["ms"] * 1e-3) / 1e12
+        st["gbs"] = st["bytes"] / (st["ms"] * 1e-3) / 1e9
+        st["bound"] = "mfma" if st["flops"] / max(st["bytes"], 1) > RIDGE else "hbm"
+    if plan.fused:
+        # one persistent launch (after a control-block reset) does all the work:
+        # it is the dominant kernel; its bytes are Q, K, V read and O written
+        # (Y is produced and consumed inside the launch)
+        dom = dict(kernel="fused_mfma_bf16", launch="forward", flops=flops, bytes=4 * tensor_b,
+                   ms=sum(per_call) / len(per_call))
+        dom["tflops"] = dom["flops"] / (dom["ms"] * 1e-3) / 1e12
+        dom["gbs"] = dom["bytes"] / (dom["ms"] * 1e-3) / 1e9
+        dom["bound"] = "mfma"
+    else:
+        dom = max(stages, key=lambda st: st["ms"])
     peak_mfma = PEAK_BF16_TFLOPS if c["dtype"] == "bf16" else PEAK_FP32_TFLOPS
     if dom["bound"] == "mfma":
         achieved, peak, unit = dom["tflops"], peak_mfma, "TFLOP/s"
@@ -231,14 +263,32 @@ def main():
         "data": "synthetic (seeded N(0,1) + 0.5 sinusoidal (t,h,w) code)" if c["pe_scale"] else "synthetic (seeded N(0,1))",
         "config": {"workload": args.config, "batch": c["batch"], "heads": c["heads"], "head_dim": c["d"],
                    "grid": list(c["grid"]), "N": info["N"], "b": info["b"], "m_tau": info["m_tau"],
-                   "tile_tokens": info["tau"], "align": c["align"], "y_dtype": "fp32" if plan.y_dtype == torch.float32 else c["dtype"],
-                   "kernels": [k1, k2]},
+                   "tile_tokens": info["tau"], "align": c["align"],
+                   "y_dtype": "fp32" if split.y_dtype == torch.float32 else c["dtype"],
+                   "fused": bool(plan.fused), "kernels": ["fused_mfma_bf16"] if plan.fused else [k1, k2]},
         "ms_per_call": round(ms_step, 4),
+        "call_ms_events": {"p10": round(pct(per_call, 0.1), 4), "p50": round(pct(per_call, 0.5), 4),
+                           "p90": round(pct(per_call, 0.9), 4)},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "flops_per_call": flops,
         "roofline": roofline,
-        "stages": [{k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in s.items()} for s in stages],
+        "stages_two_launch": [{k_: (round(v_, 4) if isinstance(v_, float) else v_) for k_, v_ in st.items()}
+                              for st in stages],
     }
+
+    # the other forward variant (fused one-launch vs two launches), for context
+    alt = mk(not plan.fused)
+    if alt.fused != plan.fused:
+        alt_ws = alt.new_workspace(dev)
+        oa = torch.empty_like(q)
+        for _ in range(2):
+            alt.forward(q, k, v, out=oa, workspace=alt_ws)
+        ta = timed(lambda: alt.forward(q, k, v, out=oa, workspace=alt_ws), args.steps)
+        out["other_variant"] = {"fused": bool(alt.fused), "ms_per_call_p50": round(pct(ta, 0.5), 4),
+                                "tflops_p50": round(flops / (pct(ta, 0.5) * 1e-3) / 1e12, 2),
+                                "bitwise_equal_to_timed_output": bool(torch.equal(oa, o))}
+        del oa, alt_ws
+    alt.close()
 
     if not args.no_dense:
         dplan = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align="dense", dtype=dt)
@@ -268,6 +318,7 @@ def main():
     else:
         out["cpu_baseline"] = None
     plan.close()
+    split.close()
     print(json.dumps(out), flush=True)
 
 

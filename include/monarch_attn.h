@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 1
+#define MONARCH_ABI_VERSION 2
 
 typedef enum monarch_status {
   MONARCH_OK = 0,
@@ -76,6 +76,13 @@ typedef enum monarch_align {
 #define MONARCH_FLAG_Y_FP32 (1u << 0)          /* keep Y in fp32 for bf16 inputs (default: bf16) */
 #define MONARCH_FLAG_ALLOW_UNALIGNED (1u << 1) /* accept a custom b that cuts a grid axis */
 #define MONARCH_FLAG_GENERIC (1u << 2)         /* force the plain VALU kernels (diagnostics) */
+/* One launch for both stages (the fused variant the explainer's kernel section describes, run
+ * as a persistent launch): stage-2 groups start as soon as the stage-1 blocks of their head and
+ * tile are done, filling the end of stage 1 instead of waiting for all of it. Used only where it
+ * applies (bf16, Y bf16, b > 128, 2 <= m_tau <= 32: the frame and tiled alignments); elsewhere
+ * the flag is ignored and monarch_plan_info.fused reports 0. It adds a small control block to
+ * the workspace. */
+#define MONARCH_FLAG_FUSED (1u << 3)
 
 typedef struct monarch_plan monarch_plan;
 
@@ -95,6 +102,7 @@ typedef struct monarch_plan_info {
   int64_t flops_stage2;  /* 4*batch*heads*N*m_tau*head_dim (0 when stage 2 is skipped, m_tau = 1) */
   int32_t stage1_kernel; /* variant id, see monarch_attn_kernel_name() */
   int32_t stage2_kernel;
+  int32_t fused;         /* 1: monarch_attn_forward makes one fused launch (MONARCH_FLAG_FUSED) */
 } monarch_plan_info;
 
 /* Validate a problem and build a plan (host only, no HIP call).
@@ -112,7 +120,8 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
 /* Free a plan (NULL is ignored). */
 void monarch_attn_destroy(monarch_plan* plan);
 
-/* Bytes of device workspace monarch_attn_forward needs (0 when b = 1 or m_tau = 1). */
+/* Bytes of device workspace monarch_attn_forward needs (0 when b = 1 or m_tau = 1): Y, plus a
+ * control block of a few hundred bytes when the plan is fused. */
 size_t monarch_attn_workspace_size(const monarch_plan* plan);
 
 /* Copy the plan's derived sizes into *info. */
@@ -122,7 +131,9 @@ monarch_status monarch_attn_plan_info(const monarch_plan* plan, monarch_plan_inf
  * stream). Asynchronous: returns after enqueueing. q, k, v, o: device pointers to
  * [batch, heads, N, head_dim] arrays of the plan's dtype. workspace: device memory of at least
  * monarch_attn_workspace_size() bytes (may be NULL when that is 0); its contents on entry are
- * ignored and on return are Y. o must not overlap q, k, v or the workspace. When m_tau = 1 the
+ * ignored and on return hold Y (and the fused control block). o must not overlap q, k, v or the
+ * workspace. A fused plan makes two launches (a control-block reset, then the fused kernel);
+ * forwards that share one workspace must not overlap in time. When m_tau = 1 the
  * second factor is the identity and stage 1 writes O directly; when b = 1 the first factor is
  * the identity and stage 2 reads V. */
 monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, const void* k,

@@ -26,7 +26,7 @@ BF16, FP32 = 0, 1
 # monarch_align
 ALIGN = {"frame": 0, "row": 1, "dense": 2, "token": 3, "custom": 4}
 # flags
-FLAG_Y_FP32, FLAG_ALLOW_UNALIGNED, FLAG_GENERIC = 1, 2, 4
+FLAG_Y_FP32, FLAG_ALLOW_UNALIGNED, FLAG_GENERIC, FLAG_FUSED = 1, 2, 4, 8
 
 EXPORTED = [
     "monarch_attn_plan", "monarch_attn_destroy", "monarch_attn_workspace_size",
@@ -44,7 +44,7 @@ class PlanInfo(ctypes.Structure):
         ("tiles", ctypes.c_int64), ("dtype", ctypes.c_int32), ("y_dtype", ctypes.c_int32),
         ("scale", ctypes.c_float), ("flags", ctypes.c_uint32), ("workspace_bytes", ctypes.c_int64),
         ("flops_stage1", ctypes.c_int64), ("flops_stage2", ctypes.c_int64),
-        ("stage1_kernel", ctypes.c_int32), ("stage2_kernel", ctypes.c_int32),
+        ("stage1_kernel", ctypes.c_int32), ("stage2_kernel", ctypes.c_int32), ("fused", ctypes.c_int32),
     ]
 
     def as_dict(self):

@@ -41,7 +41,7 @@ class MonarchPlan:
     def __init__(self, batch: int, heads: int, head_dim: int, grid: Sequence[int],
                  align: str = "frame", custom_b: int = 0, tile_tokens: Optional[int] = None,
                  dtype=torch.bfloat16, scale: Optional[float] = None, y_fp32: bool = False,
-                 allow_unaligned: bool = False, generic: bool = False):
+                 allow_unaligned: bool = False, generic: bool = False, fused: bool = False):
         L = _lib.lib()
         if isinstance(dtype, str):
             dtype = _DTYPE_NAMES[dtype]
@@ -49,7 +49,7 @@ class MonarchPlan:
             raise ValueError(f"unsupported dtype {dtype}")
         self.dtype = dtype
         flags = ((_lib.FLAG_Y_FP32 if y_fp32 else 0) | (_lib.FLAG_ALLOW_UNALIGNED if allow_unaligned else 0)
-                 | (_lib.FLAG_GENERIC if generic else 0))
+                 | (_lib.FLAG_GENERIC if generic else 0) | (_lib.FLAG_FUSED if fused else 0))
         T, H, W = (int(x) for x in grid)
         handle = ctypes.c_void_p()
         st = L.monarch_attn_plan(ctypes.byref(handle), batch, heads, head_dim, T, H, W,
@@ -69,9 +69,26 @@ class MonarchPlan:
         return int(_lib.lib().monarch_attn_workspace_size(self._h))
 
     def kernel_names(self):
+        """Kernels of stage 1 and stage 2 when run apart (monarch_attn_stage1/2)."""
         L = _lib.lib()
         return (L.monarch_attn_kernel_name(self.info["stage1_kernel"]).decode(),
                 L.monarch_attn_kernel_name(self.info["stage2_kernel"]).decode())
+
+    @property
+    def fused(self) -> bool:
+        """True when forward() makes one fused launch for both stages."""
+        return bool(self.info["fused"])
+
+    def fused_error(self, workspace: torch.Tensor) -> int:
+        """Error word of a fused plan's control block after a forward (0 = none).
+
+        Reads device memory (synchronises); for tests and diagnostics."""
+        if not self.fused:
+            return 0
+        ybytes = self.shape[0] * self.shape[1] * self.shape[2] * self.shape[3] * (
+            4 if self.y_dtype == torch.float32 else 2)
+        off = (ybytes + 255) // 256 * 256 + 8 * 4
+        return int(workspace[off:off + 4].view(torch.int32).item())
 
     @property
     def flops(self) -> int:

@@ -43,9 +43,24 @@ enum KernelId : int32_t {
   kKernelFlash = 2,     // bf16 MFMA, LDS-staged K/V tiles, online softmax, large L
   kKernelSmall = 3,     // bf16 MFMA, one wavefront per problem, L <= 32
   kKernelTiny = 4,      // VALU, D/8 lanes per problem, L <= 8, any element types
+  kKernelFused = 5,     // bf16 MFMA, both stages in one persistent launch
 };
 
 const char* kernel_name(int32_t id);
+
+// Both stages in one launch. s1: stage 1 (Q, K, V -> Y), s2: stage 2
+// (Q, K, Y -> O) of the same plan; ctl: device control block of
+// fused_ctl_ints(...) ints inside the workspace (reset by the launch).
+struct FusedArgs {
+  GroupedArgs s1, s2;
+  int* ctl;
+  int32_t tiles;  // U
+  int32_t m_tau;  // blocks per tile
+  int32_t b;      // block size
+};
+bool fused_supported(const GroupedArgs& s1, const GroupedArgs& s2);
+int64_t fused_ctl_ints(int64_t heads, int64_t tiles);
+hipError_t launch_fused(const FusedArgs& f, hipStream_t stream);
 
 // Each launcher returns hipSuccess or the launch error.
 hipError_t launch_generic(const GroupedArgs& a, hipStream_t stream);

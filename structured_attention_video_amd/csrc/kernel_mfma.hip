@@ -100,9 +100,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Only the device pass sees the builtin: instantiating it in the host pass
 // silently drops the host launch stub of the kernel that uses it, and device
 // functions never run on the host.
+template <int POLICY = 0>
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t src, char* lds, uint32_t voff) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds, 16, voff, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds, 16, voff, 0, 0, POLICY);
 #else
   (void)src; (void)lds; (void)voff;
 #endif
@@ -290,23 +291,15 @@ struct FlashState {
 
 };
 
-template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles, int nwg) {
-  using T = SwTile<D>;
-  // four separate arrays (not fields of one): the compiler then proves that
-  // reads of one slot never alias the asynchronous copy into another and
-  // waits for the copies only at the barrier
-  __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
-  __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
-  __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
-  __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
-
-  const int id = xcd_order(blockIdx.x, nwg);
-  const int qt = id % qtiles;
-  const int rest = id / qtiles;
-  const int p = rest % a.problems;
-  const int hd = rest / a.problems;
-
+// Query tile qt (128 rows) of problem p of head hd. The LDS slots are four
+// separate __shared__ arrays of the calling kernel (not fields of one): the
+// compiler then proves that reads of one slot never alias the asynchronous
+// copy into another and waits for the copies only at the barriers. Every
+// copy it issues has completed when it returns; waves whose rows lie past
+// the end of the problem return early (after the last barrier).
+template <int D, bool OUT_F32, int POLICY = 0>
+__device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, int qt, char* k0, char* k1,
+                                           char* v0, char* v1, int tid) {
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
   const int64_t base = problem_base(a, p);
   const int64_t rs = a.row_stride;
@@ -317,7 +310,7 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
   const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), base, rs, L, D,
                                OUT_F32 ? 4 : 2);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int row0 = qt * FBM + wave * 32;
   const bool active = row0 < L;
   const int n = (L + FBN - 1) / FBN;
@@ -392,7 +385,20 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float inv = 1.f / halves_sum(st.l);  // both lane halves of a row are active together
-  store_out<D, OUT_F32>(ro, row0 + (lane & 31), rs, st.o, inv, lane);
+  store_out<D, OUT_F32, POLICY>(ro, row0 + (lane & 31), rs, st.o, inv, lane);
+}
+
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles, int nwg) {
+  using T = SwTile<D>;
+  __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
+  const int id = xcd_order(blockIdx.x, nwg);
+  const int qt = id % qtiles;
+  const int rest = id / qtiles;
+  flash_tile<D, OUT_F32>(a, rest / a.problems, rest % a.problems, qt, k0, k1, v0, v1, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- group
@@ -529,6 +535,164 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(Grouped
   }
 }
 
+// ---------------------------------------------------------------- fused
+// Both stages in one persistent launch. Work items are stage-1 query tiles
+// (as flash_kernel) and stage-2 chunks of kFusedGroups groups (m_tau <= 32
+// rows each). Each XCD owns a contiguous share of both lists and hands its
+// items out in order through its own ticket counter, stage-1 tiles first, so
+// the query tiles of one problem stay on one XCD (shared L2) and a workgroup
+// that draws a stage-2 chunk knows that every stage-1 tile of its XCD has
+// already been drawn by a running workgroup.
+//
+// Y crosses XCDs, whose L2 caches are not coherent with one another. It is
+// written with device-scope stores (written through the L2) and read with
+// device-scope loads, so no L2 writeback or invalidation is needed (each
+// costs a whole-L2 operation). A stage-1 tile counts itself in ready[head,
+// tile] once its Y stores have completed; a stage-2 chunk waits until its
+// (head, tile) counter reaches m_tau * qtiles before loading Y. The wait
+// always ends: every tile it counts has been drawn by a workgroup that is
+// running or done, and stage-1 tiles never wait. A spin bound (far above any
+// legitimate wait) sets an error word instead of hanging if that were ever
+// violated (e.g. an XCD with no workgroups).
+//
+// Control block (ints): [0, 8) tickets per XCD, [8] error, [16, ...) ready.
+constexpr int kFusedXcds = 8;
+constexpr int kFusedGroups = 16;  // stage-2 groups per work item, 4 per wave
+constexpr int kCtlError = 8;
+constexpr int kCtlReady = 16;
+
+__global__ void __launch_bounds__(256) fused_reset(int* ctl, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) ctl[i] = 0;
+}
+
+// One stage-2 group (2 <= L <= 32 rows) by one wave: K and Y rows copied into
+// this wave's LDS (two swizzled 32-row tiles), the Q fragment read directly,
+// one pass, O written directly.
+template <int D>
+__device__ __forceinline__ void group_wave(const GroupedArgs& a, int hd, int p, char* kl, char* vl,
+                                           const FlashOffsets<D>& fo, int lane) {
+  constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB;
+  const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
+  const int64_t base = problem_base(a, p);
+  const int64_t rs = a.row_stride;
+  const int L = a.L, h = lane >> 5;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
+  const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
+  const auto ro = problem_rsrc(static_cast<const bf16*>(a.o) + hoff, base, rs, L, D, 2);
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / CPR;
+    const int c = (lane % CPR) ^ swz<D>(row);
+    const uint32_t goff = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
+    lds_dma16(rk, kl + RPI * i * ROWB, goff);
+    lds_dma16<kPolicyDevice>(rv, vl + RPI * i * ROWB, goff);  // Y, written by other XCDs
+  }
+  bf16x8 qf[D / 16];
+  load_qfrag<D>(qf, rq, 0, rs, lane);
+  wait_dma();
+  f32x16 s = {};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) s = mma(ld_bf16x8(kl + fo.k[ks]), qf[ks], s);
+  const float c = a.scale_log2;
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    if (acc_key(i, h) >= L) s[i] = -INFINITY;
+    mx = fmaxf(mx, s[i]);
+  }
+  mx = halves_max(mx) * c;
+  float l = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = fast_exp2(fmaf(s[i], c, -mx));
+    l += s[i];
+  }
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) o[mt] = f32x16{};
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    const bf16x8 pb = p_operand(s, st);
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) o[mt] = mma(v_operand<D>(vl, fo, mt, st), pb, o[mt]);
+  }
+  store_out<D, false>(ro, lane & 31, rs, o, 1.f / halves_sum(l), lane);
+}
+
+template <int D>
+__global__ void __launch_bounds__(FNT, 2) fused_kernel(FusedArgs f, int qtiles, int nchunks, int nxcd) {
+  using T = SwTile<D>;
+  __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
+  __shared__ int ticket;
+
+  const int tid = threadIdx.x;
+  // hardware XCD of this workgroup (HW_REG_XCC_ID, bits 3:0)
+  const int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % nxcd;
+  const int64_t n1 = static_cast<int64_t>(qtiles) * f.s1.problems * f.s1.heads;
+  const int64_t n2 = static_cast<int64_t>(nchunks) * f.tiles * f.s2.heads;
+  const int b1 = static_cast<int>(n1 * xcd / nxcd), c1 = static_cast<int>(n1 * (xcd + 1) / nxcd) - b1;
+  const int b2 = static_cast<int>(n2 * xcd / nxcd), c2 = static_cast<int>(n2 * (xcd + 1) / nxcd) - b2;
+  const int target = f.m_tau * qtiles;
+  int* ready = f.ctl + kCtlReady;
+  int acquired = -1;
+
+  for (;;) {
+    __syncthreads();  // LDS slots and `ticket` are free again
+    if (tid == 0) ticket = atomicAdd(f.ctl + xcd, 1);
+    __syncthreads();
+    const int t = ticket;
+    if (t >= c1 + c2) break;
+    // the thread index passed on is made opaque, so the per-lane offsets of
+    // each item are computed inside it instead of being hoisted out of this
+    // loop and kept live (in spilled registers) across both kinds of item
+    int otid = tid;
+    asm volatile("" : "+v"(otid));
+    if (t < c1) {
+      const int id = b1 + t;
+      const int qt = id % qtiles, rest = id / qtiles;
+      const int p = rest % f.s1.problems, hd = rest / f.s1.problems;
+      flash_tile<D, false, kPolicyDevice>(f.s1, hd, p, qt, k0, k1, v0, v1, otid);
+      wait_dma();  // this wave's written-through Y stores have completed
+      __syncthreads();
+      if (tid == 0)
+        __hip_atomic_fetch_add(ready + hd * f.tiles + p / f.m_tau, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      const int id = b2 + (t - c1);
+      const int chunk = id % nchunks, rest = id / nchunks;
+      const int u = rest % f.tiles, hd = rest / f.tiles;
+      const int key = hd * f.tiles + u;
+      if (key != acquired) {
+        if (tid == 0) {
+          int spins = 0;
+          while (__hip_atomic_load(ready + key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(8);
+            if (++spins > (1 << 20)) {
+              __hip_atomic_store(f.ctl + kCtlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              break;
+            }
+          }
+        }
+        __syncthreads();  // Y is read below with device-coherent loads only
+        acquired = key;
+      }
+      const int w = otid >> 6;
+      char* const lds_wave = w == 0 ? k0 : w == 1 ? k1 : w == 2 ? v0 : v1;
+      const FlashOffsets<D> fo(w, otid & 63, f.s2.row_stride);
+      const int j0 = chunk * kFusedGroups;
+#pragma unroll 1
+      for (int g = w; g < kFusedGroups; g += 4) {
+        const int j = j0 + g;
+        if (j >= f.b) break;
+        group_wave<D>(f.s2, hd, u * f.b + j, lds_wave, lds_wave + 32 * 2 * D, fo, otid & 63);
+      }
+    }
+  }
+}
+
 bool mfma_types_ok(const GroupedArgs& a) {
   return (a.D == 64 || a.D == 128) && a.qk_type == kBF16 && a.v_type == kBF16;
 }
@@ -578,6 +742,35 @@ hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
   const bool f32 = a.o_type == kF32;
   if (a.D == 128) return f32 ? launch_flash_t<128, true>(a, s) : launch_flash_t<128, false>(a, s);
   return f32 ? launch_flash_t<64, true>(a, s) : launch_flash_t<64, false>(a, s);
+}
+
+bool fused_supported(const GroupedArgs& s1, const GroupedArgs& s2) {
+  return flash_supported(s1) && s1.o_type == kBF16 && mfma_types_ok(s2) && s2.o_type == kBF16 && s2.D == s1.D &&
+         s2.L >= 2 && s2.L <= 32 && offsets_fit(s2, 32);
+}
+
+int64_t fused_ctl_ints(int64_t heads, int64_t tiles) { return kCtlReady + heads * tiles; }
+
+hipError_t launch_fused(const FusedArgs& f, hipStream_t s) {
+  if (!fused_supported(f.s1, f.s2) || !f.ctl) return hipErrorInvalidValue;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  // XCDs of 32 CUs each on this part (8 on the full device)
+  const int nxcd = cus >= 32 * kFusedXcds ? kFusedXcds : (cus >= 32 ? cus / 32 : 1);
+  const int qtiles = (f.s1.L + FBM - 1) / FBM;
+  const int nchunks = (f.b + kFusedGroups - 1) / kFusedGroups;
+  const int64_t nctl = fused_ctl_ints(f.s1.heads, f.tiles);
+  hipLaunchKernelGGL(fused_reset, dim3(1), dim3(256), 0, s, f.ctl, static_cast<int>(nctl));
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = 2 * (cus > 0 ? cus : 1);  // two resident workgroups per CU
+  if (f.s1.D == 128)
+    hipLaunchKernelGGL((fused_kernel<128>), dim3(grid), dim3(FNT), 0, s, f, qtiles, nchunks, nxcd);
+  else
+    hipLaunchKernelGGL((fused_kernel<64>), dim3(grid), dim3(FNT), 0, s, f, qtiles, nchunks, nxcd);
+  return hipGetLastError();
 }
 
 bool small_supported(const GroupedArgs& a) {

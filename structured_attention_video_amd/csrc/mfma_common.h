@@ -149,7 +149,12 @@ __device__ __forceinline__ bf16x8 p_operand(const f32x16& p, int half) {
 // Write one lane's share of O (query row `row` of the problem, all D
 // channels) from O^T accumulators through the problem's descriptor (rows past
 // the end are dropped). Channel of register i in tile mt is 32*mt + acc_key(i, h).
-template <int D, bool OUT_F32>
+// Cache-policy operand of buffer instructions: SC1 (bit 4) makes an access
+// coherent at device scope on gfx950 (a store is written through the
+// per-XCD L2, a load does not use a possibly stale L2 line).
+constexpr int kPolicyDevice = 16;
+
+template <int D, bool OUT_F32, int POLICY = 0>
 __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t ro, int row, int64_t rs, const f32x16 (&o)[D / 32],
                                           float inv, int lane) {
   const int h = lane >> 5;
@@ -164,12 +169,12 @@ __device__ __forceinline__ void store_out(__amdgpu_buffer_rsrc_t ro, int row, in
         u32x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = __float_as_uint(o[mt][4 * g + e] * inv);
-        __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(off), 0, POLICY);
       } else {
         bf16x4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(o[mt][4 * g + e] * inv);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, static_cast<int>(off), 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), ro, static_cast<int>(off), 0, POLICY);
       }
     }
   }

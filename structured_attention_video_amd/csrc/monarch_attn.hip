@@ -18,7 +18,8 @@ struct monarch_plan {
 namespace {
 
 constexpr uint32_t kKnownFlags =
-    MONARCH_FLAG_Y_FP32 | MONARCH_FLAG_ALLOW_UNALIGNED | MONARCH_FLAG_GENERIC;
+    MONARCH_FLAG_Y_FP32 | MONARCH_FLAG_ALLOW_UNALIGNED | MONARCH_FLAG_GENERIC | MONARCH_FLAG_FUSED;
+
 
 size_t elem_bytes(int32_t dt) { return dt == MONARCH_FP32 ? 4 : 2; }
 
@@ -27,6 +28,9 @@ int64_t tensor_bytes(const monarch_plan_info& p, int32_t dt) {
 }
 
 ElemType as_elem(int32_t dt) { return dt == MONARCH_FP32 ? kF32 : kBF16; }
+
+// The fused control block follows Y in the workspace, 256-byte aligned.
+int64_t ctl_offset(const monarch_plan_info& p) { return (tensor_bytes(p, p.y_dtype) + 255) / 256 * 256; }
 
 // Grouped-attention description of stage 1 (contiguous blocks of b tokens).
 GroupedArgs stage1_args(const monarch_plan_info& p, const void* q, const void* k, const void* v,
@@ -168,6 +172,15 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
     GroupedArgs a = stage2_args(i, nullptr, nullptr, nullptr, has1 ? i.y_dtype : dtype, nullptr);
     i.stage2_kernel = choose_kernel(a, flags);
   }
+  i.fused = 0;
+  if ((flags & MONARCH_FLAG_FUSED) && !(flags & MONARCH_FLAG_GENERIC) && has1 && has2) {
+    const GroupedArgs a1 = stage1_args(i, nullptr, nullptr, nullptr, nullptr, i.y_dtype);
+    const GroupedArgs a2 = stage2_args(i, nullptr, nullptr, nullptr, i.y_dtype, nullptr);
+    if (fused_supported(a1, a2)) {
+      i.fused = 1;
+      i.workspace_bytes = ctl_offset(i) + fused_ctl_ints(BH, i.tiles) * static_cast<int64_t>(sizeof(int));
+    }
+  }
   *out = p;
   return MONARCH_OK;
 }
@@ -217,6 +230,16 @@ monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, con
   const bool has1 = p.b > 1, has2 = p.m_tau > 1;
   if (!has2) return run_stage1(p, q, k, v, o, p.dtype, s);  // second factor is the identity
   if (!has1) return run_stage2(p, q, k, v, p.dtype, o, s);  // first factor is the identity: Y = V
+  if (p.fused) {
+    FusedArgs f{};
+    f.s1 = stage1_args(p, q, k, v, workspace, p.y_dtype);
+    f.s2 = stage2_args(p, q, k, workspace, p.y_dtype, o);
+    f.ctl = reinterpret_cast<int*>(static_cast<char*>(workspace) + ctl_offset(p));
+    f.tiles = static_cast<int32_t>(p.tiles);
+    f.m_tau = static_cast<int32_t>(p.m_tau);
+    f.b = static_cast<int32_t>(p.b);
+    return launch_fused(f, s) == hipSuccess ? MONARCH_OK : MONARCH_ERR_HIP;
+  }
   monarch_status st = run_stage1(p, q, k, v, workspace, p.y_dtype, s);
   if (st != MONARCH_OK) return st;
   return run_stage2(p, q, k, workspace, p.y_dtype, o, s);
@@ -274,6 +297,7 @@ const char* kernel_name(int32_t id) {
     case kKernelFlash: return "flash_mfma_bf16";
     case kKernelSmall: return "small_group_mfma_bf16";
     case kKernelTiny: return "tiny_group_valu";
+    case kKernelFused: return "fused_mfma_bf16";
   }
   return "unknown";
 }

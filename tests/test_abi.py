@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.monarch_attn_abi_version() == 1
+    assert L.monarch_attn_abi_version() == 2
 
 
 def _plan(batch=1, heads=2, d=128, grid=(4, 6, 10), align=0, custom_b=0, tile=0, dtype=0,
@@ -184,3 +184,44 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64)
     with pytest.raises(ValueError):
         p.forward(x, x, x)
+
+
+# ------------------------------------------------------------------ fused plans
+def _info(**kw):
+    st, h = _plan(**kw)
+    assert st == _lib.OK
+    info = _lib.PlanInfo()
+    assert L.monarch_attn_plan_info(h, ctypes.byref(info)) == _lib.OK
+    ws = L.monarch_attn_workspace_size(h)
+    L.monarch_attn_destroy(h)
+    return info, ws
+
+
+def test_fused_plan_applies_to_frame_and_tiled_bf16():
+    # frame 21x30x52: b = 1560 > 128 (flash stage 1), m = 21 <= 32 (one-wave groups)
+    info, ws = _info(heads=12, grid=(21, 30, 52), flags=_lib.FLAG_FUSED)
+    assert info.fused == 1
+    y = 12 * 32760 * 128 * 2
+    assert ws == (y + 255) // 256 * 256 + (16 + 12 * 1) * 4
+    # the separate stages keep their own kernels (stage1/stage2 entry points)
+    assert L.monarch_attn_kernel_name(info.stage1_kernel) == b"flash_mfma_bf16"
+    info, ws = _info(heads=12, grid=(21, 30, 52), tile=4680, flags=_lib.FLAG_FUSED)
+    assert info.fused == 1 and info.tiles == 7
+    assert ws == (y + 255) // 256 * 256 + (16 + 12 * 7) * 4
+    assert L.monarch_attn_kernel_name(5) == b"fused_mfma_bf16"
+
+
+@pytest.mark.parametrize("kw", [
+    dict(heads=12, grid=(21, 30, 52), align=1),                          # row: b = 52 (group stage 1)
+    dict(heads=12, grid=(81, 30, 52)),                                   # m = 81 > 32
+    dict(heads=2, grid=(21, 30, 52), dtype=1),                           # fp32
+    dict(heads=2, grid=(21, 30, 52), flags=_lib.FLAG_Y_FP32),            # Y fp32
+    dict(heads=2, grid=(21, 30, 52), flags=_lib.FLAG_GENERIC),           # diagnostics path
+    dict(heads=2, grid=(21, 30, 52), align=2),                           # dense: no stage 2
+], ids=["row", "m81", "fp32", "y_fp32", "generic", "dense"])
+def test_fused_flag_ignored_where_it_does_not_apply(kw):
+    flags = kw.pop("flags", 0) | _lib.FLAG_FUSED
+    info, ws = _info(flags=flags, **kw)
+    assert info.fused == 0
+    plain, ws_plain = _info(flags=flags & ~_lib.FLAG_FUSED, **kw)
+    assert ws == ws_plain
