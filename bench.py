@@ -12,7 +12,8 @@ Prints ONE JSON line. Besides the contract fields it carries:
   cpu_baseline  the fp64 oracle timed on a bounded sample on the host cores;
   stages_two_launch  per-stage ms and rates of the two-launch path (stage 1
                 then stage 2), timed separately; dense: the library's own
-                dense softmax-attention kernel at the same shape.
+                dense softmax-attention kernel at the same shape; backward:
+                the gradient pass at the same shape.
 A call is stage 1 then stage 2 (two launches); --fused auto/on times the
 library's one-launch fused variant instead where it applies (frame and tiled
 alignments). call_ms_events: per-call device time from HIP events in a second
@@ -289,6 +290,23 @@ def main():
                                 "bitwise_equal_to_timed_output": bool(torch.equal(oa, o))}
         del oa, alt_ws
     alt.close()
+
+    # the backward pass (gradients of all three inputs) at the same shape, for context:
+    # time per call and the rate at 2.5x the forward FLOPs (five products of the
+    # forward's size: the usual accounting for attention backward; the library
+    # additionally recomputes the forward)
+    if split.backward_workspace_bytes:
+        bws = torch.empty(split.backward_workspace_bytes, dtype=torch.uint8, device=dev)
+        go = torch.randn(q.shape, generator=torch.Generator().manual_seed(77)).to(dt).to(dev)
+        gq, gk, gv = (torch.empty_like(q) for _ in range(3))
+        ob = split.forward(q, k, v)
+        for _ in range(2):
+            split.backward(q, k, v, ob, go, workspace=bws, grads=(gq, gk, gv))
+        tb = timed(lambda: split.backward(q, k, v, ob, go, workspace=bws, grads=(gq, gk, gv)),
+                   max(3, args.steps // 5))
+        out["backward"] = {"ms_per_call_p50": round(pct(tb, 0.5), 4),
+                           "tflops_at_2p5x_forward": round(2.5 * flops / (pct(tb, 0.5) * 1e-3) / 1e12, 2)}
+        del bws, go, gq, gk, gv, ob
 
     if not args.no_dense:
         dplan = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align="dense", dtype=dt)

@@ -153,6 +153,23 @@ monarch_status monarch_attn_stage1(const monarch_plan* plan, const void* q, cons
 monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, const void* k,
                                    const void* y, void* o, void* stream);
 
+/* Bytes of device workspace monarch_attn_backward needs (0 when the plan has no backward:
+ * fp32 plans and MONARCH_FLAG_GENERIC plans). Independent of the forward's workspace. */
+size_t monarch_attn_backward_workspace_size(const monarch_plan* plan);
+
+/* Gradients of the Monarch forward (the chain rule through both softmax stages; the explainer's
+ * section 2.C ships forward and backward kernels for fine-tuning): given O = forward(Q, K, V)
+ * and grad_o = dL/dO, writes grad_q = dL/dQ, grad_k = dL/dK, grad_v = dL/dV. All nine arrays are
+ * [batch, heads, N, head_dim] bf16 device arrays (bf16 plans only; fp32 plans return
+ * MONARCH_ERR_UNSUPPORTED); o must be the output of monarch_attn_forward for the same inputs.
+ * Stage 1 is recomputed (Y and per-row softmax statistics of both stages go to the workspace,
+ * whose contents on entry are ignored), then the stage-2 backward and the stage-1 backward run,
+ * fp32 accumulation throughout; Q and K receive the sum of both stages' gradients. grad_* must
+ * not overlap each other, the inputs or the workspace. Asynchronous on `stream`. */
+monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                     const void* o, const void* grad_o, void* grad_q, void* grad_k,
+                                     void* grad_v, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* monarch_status_string(monarch_status status);
 

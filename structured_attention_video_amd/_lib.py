@@ -32,7 +32,7 @@ EXPORTED = [
     "monarch_attn_plan", "monarch_attn_destroy", "monarch_attn_workspace_size",
     "monarch_attn_plan_info", "monarch_attn_forward", "monarch_attn_stage1",
     "monarch_attn_stage2", "monarch_status_string", "monarch_attn_kernel_name",
-    "monarch_attn_abi_version",
+    "monarch_attn_abi_version", "monarch_attn_backward_workspace_size", "monarch_attn_backward",
 ]
 
 
@@ -87,5 +87,9 @@ def lib() -> ctypes.CDLL:
     L.monarch_attn_kernel_name.restype = ctypes.c_char_p
     L.monarch_attn_abi_version.argtypes = []
     L.monarch_attn_abi_version.restype = i32
+    L.monarch_attn_backward_workspace_size.argtypes = [vp]
+    L.monarch_attn_backward_workspace_size.restype = sz
+    L.monarch_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.monarch_attn_backward.restype = i32
     _lib = L
     return L

@@ -147,6 +147,30 @@ class MonarchPlan:
         _check(st, "monarch_attn_stage2")
         return out
 
+    @property
+    def backward_workspace_bytes(self) -> int:
+        """Workspace bytes of backward() (0: this plan has no backward)."""
+        return int(_lib.lib().monarch_attn_backward_workspace_size(self._h))
+
+    def backward(self, q, k, v, o, grad_o, workspace=None, grads=None):
+        """(dL/dQ, dL/dK, dL/dV) for O = forward(q, k, v) and grad_o = dL/dO."""
+        self._check_io(q, k, v, o, grad_o)
+        for t in (q, k, v, o, grad_o):
+            if t.dtype != self.dtype:
+                raise ValueError(f"dtype {t.dtype} != plan dtype {self.dtype}")
+        if grads is None:
+            grads = tuple(torch.empty_like(q) for _ in range(3))
+        self._check_io(*grads)
+        n = self.backward_workspace_bytes
+        if workspace is None:
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        ws_n = workspace.numel() * workspace.element_size()
+        st = _lib.lib().monarch_attn_backward(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                              grad_o.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
+                                              grads[2].data_ptr(), workspace.data_ptr(), ws_n, self._stream(q))
+        _check(st, "monarch_attn_backward")
+        return grads
+
     def close(self):
         if getattr(self, "_h", None):
             _lib.lib().monarch_attn_destroy(self._h)

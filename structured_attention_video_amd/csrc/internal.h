@@ -34,7 +34,36 @@ struct GroupedArgs {
   ElemType qk_type;
   ElemType v_type;
   ElemType o_type;
+  float* lse;         // optional (bf16 MFMA and tiny kernels): per query row, log2 of the
+                      // softmax denominator in the exp2 domain, i.e. the row's probabilities
+                      // are exp2(scale_log2 * <q,k> - lse); indexed [head][token]
 };
+
+// Backward of one grouped-attention stage (the chain rule of O = P V with
+// P = rowsoftmax(s Q K^T)): dQ = s dS K, dK = s dS^T Q, dV = P^T G with
+// dS = P * (G V^T - delta). g: the forward's problem geometry and inputs
+// (v = the stage's values); go: G, the gradient of the stage output, same
+// layout as q; lse: the forward's per-row statistic (see GroupedArgs::lse);
+// delta: per row, the sum over channels of G * O. Outputs are written in
+// their element types; dq_in / dk_in (optional, fp32, same layout) are added
+// before the store. Per-row arrays are indexed [head][token].
+struct BwdArgs {
+  GroupedArgs g;
+  const void* go;
+  const float* lse;
+  const float* delta;
+  void* dq;
+  void* dk;
+  void* dv;
+  const float* dq_in;
+  const float* dk_in;
+  ElemType dq_type, dk_type, dv_type;
+};
+bool bwd_supported(const GroupedArgs& g);
+hipError_t launch_bwd(const BwdArgs& b, hipStream_t stream);
+// out[r] = sum_c a[r][c] * b[r][c] over rows x D (bf16 or fp32 elements)
+hipError_t launch_rowdot(const void* a, ElemType ta, const void* b, ElemType tb, float* out, int64_t rows, int D,
+                         hipStream_t stream);
 
 // Kernel variant ids (reported through the plan info).
 enum KernelId : int32_t {

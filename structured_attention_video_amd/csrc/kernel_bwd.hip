@@ -1,0 +1,357 @@
+// Backward of one grouped-attention stage on the matrix cores (bf16 inputs,
+// fp32 accumulation), by recomputation from the forward's per-row log-sum-
+// exp statistic, in two kernels that share no accumulator, so no atomics:
+//
+// bwd_dq: a workgroup of 4 waves owns 128 query rows of one problem (as the
+//   forward's flash kernel) and streams the problem's K and V in 64-row
+//   tiles through LDS. Per tile: S^T = K Q^T and dP^T = V G^T (V rows are
+//   read exactly like K rows, G is held like Q), P^T = exp2(c S^T - lse),
+//   dS^T = P^T * (dP^T - delta), and dQ^T += K^T dS^T, where the K^T operand
+//   is gathered by the transposing LDS reads the forward uses for V^T and
+//   dS^T leaves the accumulator already in B-operand layout (as P^T does in
+//   the forward).
+// bwd_dkdv (launched twice: dV, then dK): a workgroup owns 128 key rows of
+//   one problem (32 per wave, K and V held as B operands) and streams the
+//   problem's Q and G in 64-row tiles through LDS, with lse and delta of
+//   those rows. Per 32-query step: S = Q K^T and dP = G V^T (lane = key), P
+//   and dS as above, then dV^T += G^T P or dK^T += Q^T dS with G^T and Q^T
+//   gathered by transposing reads, P and dS again straight from the
+//   accumulators.
+//
+// Rows past the end of a problem read as zero through the buffer
+// descriptors; keys past the end get score -inf in the last tile of
+// bwd_dq; queries past the end have zero Q and G rows and delta 0, so their
+// terms in dK and dV vanish. (The chain rule itself: explainer section 2.C
+// ships forward and backward kernels; the formulas are those of softmax
+// attention, applied to each Monarch stage.)
+#include "flash_common.h"
+
+namespace monarch {
+namespace {
+
+// P = exp2(c s - lse) and dS = P * (dp - delta), in place (s -> P, dp -> dS)
+__device__ __forceinline__ void probs_grads(f32x16& s, f32x16& dp, const float (&lse)[16], const float (&del)[16],
+                                            float c) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s[i] = fast_exp2(fmaf(s[i], c, -lse[i]));
+    dp[i] = s[i] * (dp[i] - del[i]);
+  }
+}
+
+// Store a lane's share of X^T accumulators (channels in registers, rows in
+// lanes: row `row` of the problem) scaled by `mul`, plus the fp32 `add` rows.
+template <int D>
+__device__ __forceinline__ void store_rows(__amdgpu_buffer_rsrc_t ro, bool out_f32, __amdgpu_buffer_rsrc_t ra,
+                                           bool has_add, int row, int64_t rs, const f32x16 (&x)[D / 32], float mul,
+                                           int lane) {
+  const int h = lane >> 5;
+  const uint32_t rowel = static_cast<uint32_t>(row * rs * D);
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t ch = 32 * mt + 8 * g + 4 * h;
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = x[mt][4 * g + e] * mul;
+      if (has_add) {
+        const u32x4 a = bload16(ra, (rowel + ch) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] += __uint_as_float(a[e]);
+      }
+      if (out_f32) {
+        const u32x4 w = {__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, ro, static_cast<int>((rowel + ch) * 4), 0, 0);
+      } else {
+        bf16x4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = static_cast<bf16>(v[e]);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), ro, static_cast<int>((rowel + ch) * 2), 0, 0);
+      }
+    }
+  }
+}
+
+// S^T (or dP^T) of one 64-row tile against a wave's fragment f: two 32-row
+// accumulator chains from the row-major tile t
+template <int D>
+__device__ __forceinline__ void tile_products(f32x16 (&s)[2], const char* t, const FlashOffsets<D>& fo,
+                                              const bf16x8 (&f)[D / 16]) {
+  s[0] = f32x16{};
+  s[1] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    s[0] = mma(k_operand<D>(t, fo, ks, 0), f[ks], s[0]);
+    s[1] = mma(k_operand<D>(t, fo, ks, 1), f[ks], s[1]);
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(FNT, 2) bwd_dq_kernel(BwdArgs b, int qtiles, int nwg) {
+  using T = SwTile<D>;
+  __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
+  const GroupedArgs& a = b.g;
+  const int id = xcd_order(blockIdx.x, nwg);
+  const int qt = id % qtiles, rest = id / qtiles;
+  const int p = rest % a.problems, hd = rest / a.problems;
+  const int64_t ntok = a.head_elems / D;
+  const int64_t hoff = hd * a.head_elems;
+  const int64_t base = problem_base(a, p);
+  const int64_t rs = a.row_stride;
+  const int L = a.L;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
+  const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
+  const auto rg = problem_rsrc(static_cast<const bf16*>(b.go) + hoff, base, rs, L, D, 2);
+  const bool f32 = b.dq_type == kF32;
+  const auto ro = problem_rsrc(static_cast<const char*>(b.dq) + hoff * (f32 ? 4 : 2), base, rs, L, D, f32 ? 4 : 2);
+  const auto ra = problem_rsrc(b.dq_in ? b.dq_in + hoff : b.delta, base, rs, L, D, 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int row0 = qt * FBM + wave * 32;
+  const int r = row0 + (lane & 31);
+  const int n = (L + FBN - 1) / FBN;
+  const int nv_last = L - (n - 1) * FBN;
+  const float c = a.scale_log2;
+  const FlashOffsets<D> fo(wave, lane, rs);
+  const uint32_t tile_bytes = static_cast<uint32_t>(FBN * rs * D * 2);
+
+  fo.dma(k0, rk, 0, wave);
+  fo.dma(v0, rv, 0, wave);
+  bf16x8 qf[D / 16], gf[D / 16];
+  load_qfrag<D>(qf, rq, row0, rs, lane);
+  load_qfrag<D>(gf, rg, row0, rs, lane);
+  const float lse_r = r < L ? b.lse[hd * ntok + base + r * rs] : 0.f;
+  const float del_r = r < L ? b.delta[hd * ntok + base + r * rs] : 0.f;
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+  wait_dma();
+  __syncthreads();
+
+  auto step = [&](int j, const char* kc, const char* vc, char* kn, char* vn) {
+    if (j + 1 < n) {
+      fo.dma(kn, rk, (j + 1) * tile_bytes, wave);
+      fo.dma(vn, rv, (j + 1) * tile_bytes, wave);
+    }
+    f32x16 s[2], dp[2];
+    tile_products<D>(s, kc, fo, qf);
+    tile_products<D>(dp, vc, fo, gf);
+    if (j == n - 1 && nv_last < FBN) mask_tail(s, nv_last, h);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[t][i] = fast_exp2(fmaf(s[t][i], c, -lse_r));
+        dp[t][i] = s[t][i] * (dp[t][i] - del_r);
+      }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const bf16x8 pb = p_operand(dp[st >> 1], st & 1);
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mma(v_operand<D>(kc, fo, mt, st), pb, dq[mt]);
+    }
+    wait_dma();
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < n; j += 2) {
+    step(j, k0, v0, k1, v1);
+    step(j + 1, k1, v1, k0, v0);
+  }
+  if (j < n) step(j, k0, v0, k1, v1);
+
+  // dQ = s * dS K, where s = scale_log2 / log2(e)
+  store_rows<D>(ro, f32, ra, b.dq_in != nullptr, r, rs, dq, c * 0.6931471805599453f, lane);
+}
+
+// MODE 0: dV only (S -> P; dV^T += G^T P). MODE 1: dK only (S, dP -> dS;
+// dK^T += Q^T dS). One kernel holding both accumulators, K and V would need
+// more registers than two waves per SIMD have; recomputing S in both costs
+// a quarter more matrix work instead.
+template <int D, int MODE>
+__global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles, int nwg) {
+  using T = SwTile<D>;
+  __shared__ __attribute__((aligned(1024))) char q0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char q1[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char g0[T::bytes];
+  __shared__ __attribute__((aligned(1024))) char g1[T::bytes];
+  __shared__ __attribute__((aligned(16))) float st_lse[2][FBN];
+  __shared__ __attribute__((aligned(16))) float st_del[2][FBN];
+  const GroupedArgs& a = b.g;
+  const int id = xcd_order(blockIdx.x, nwg);
+  const int kt = id % ktiles, rest = id / ktiles;
+  const int p = rest % a.problems, hd = rest / a.problems;
+  const int64_t ntok = a.head_elems / D;
+  const int64_t hoff = hd * a.head_elems;
+  const int64_t base = problem_base(a, p);
+  const int64_t rs = a.row_stride;
+  const int L = a.L;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
+  const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
+  const auto rg = problem_rsrc(static_cast<const bf16*>(b.go) + hoff, base, rs, L, D, 2);
+  const bool kf32 = b.dk_type == kF32, vf32 = b.dv_type == kF32;
+  const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * (kf32 ? 4 : 2), base, rs, L, D, kf32 ? 4 : 2);
+  const auto rdv = problem_rsrc(static_cast<const char*>(b.dv) + hoff * (vf32 ? 4 : 2), base, rs, L, D, vf32 ? 4 : 2);
+  const auto ra = problem_rsrc(b.dk_in ? b.dk_in + hoff : b.delta, base, rs, L, D, 4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int key0 = kt * FBM + wave * 32;
+  const int n = (L + FBN - 1) / FBN;
+  const float c = a.scale_log2;
+  const FlashOffsets<D> fo(wave, lane, rs);
+  const uint32_t tile_bytes = static_cast<uint32_t>(FBN * rs * D * 2);
+  const float* lse_h = b.lse + hd * ntok + base;
+  const float* del_h = b.delta + hd * ntok + base;
+
+  // per-row statistics of query tile j (rows past the end: 0), loaded into
+  // registers early and stored to LDS slot s just before the barrier
+  float nl = 0.f, nd = 0.f;
+  auto stats_load = [&](int j) {
+    if (tid < FBN) {
+      const int q = j * FBN + tid;
+      nl = q < L ? lse_h[q * rs] : 0.f;
+      nd = q < L ? del_h[q * rs] : 0.f;
+    }
+  };
+  auto stats_store = [&](int s) {
+    if (tid < FBN) {
+      st_lse[s][tid] = nl;
+      st_del[s][tid] = nd;
+    }
+  };
+  fo.dma(q0, rq, 0, wave);
+  fo.dma(g0, rg, 0, wave);
+  stats_load(0);
+  stats_store(0);
+  bf16x8 kf[D / 16], vf[D / 16];
+  load_qfrag<D>(kf, rk, key0, rs, lane);
+  if (MODE == 1) load_qfrag<D>(vf, rv, key0, rs, lane);
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) acc[mt] = f32x16{};
+  wait_dma();
+  __syncthreads();
+
+  auto step = [&](int j, const char* qc, const char* gc, char* qn, char* gn, int sc) {
+    if (j + 1 < n) {
+      fo.dma(qn, rq, (j + 1) * tile_bytes, wave);
+      fo.dma(gn, rg, (j + 1) * tile_bytes, wave);
+      stats_load(j + 1);
+    }
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      // S = Q K^T, dP = G V^T for 32 queries: lane = key, register i = query
+      // 32*sub + 8*(i/4) + 4*h + i%4 of the tile
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = mma(k_operand<D>(qc, fo, ks, sub), kf[ks], s);
+        if (MODE == 1) dp = mma(k_operand<D>(gc, fo, ks, sub), vf[ks], dp);
+      }
+      float lse[16], del[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int q = 32 * sub + 8 * g + 4 * h;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lse[4 * g + e] = st_lse[sc][q + e];
+          del[4 * g + e] = MODE == 1 ? st_del[sc][q + e] : 0.f;
+        }
+      }
+      probs_grads(s, dp, lse, del, c);
+      // dV^T += G^T P (MODE 0) or dK^T += Q^T dS (MODE 1), two 16-query steps
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 pb = p_operand(MODE == 1 ? dp : s, st);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt)
+          acc[mt] = mma(v_operand<D>(MODE == 1 ? qc : gc, fo, mt, 2 * sub + st), pb, acc[mt]);
+      }
+    }
+    if (j + 1 < n) stats_store(sc ^ 1);
+    wait_dma();
+    __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < n; j += 2) {
+    step(j, q0, g0, q1, g1, 0);
+    step(j + 1, q1, g1, q0, g0, 1);
+  }
+  if (j < n) step(j, q0, g0, q1, g1, 0);
+
+  const int r = key0 + (lane & 31);
+  if (MODE == 1) store_rows<D>(rdk, kf32, ra, b.dk_in != nullptr, r, rs, acc, c * 0.6931471805599453f, lane);
+  else store_rows<D>(rdv, vf32, ra, false, r, rs, acc, 1.f, lane);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) rowdot_kernel(const void* a, int ta, const void* bp, int tb, float* out,
+                                                     int64_t rows) {
+  // D/8 lanes per row, 8 channels each, reduced across the row's lanes
+  constexpr int LP = D / 8;
+  const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / LP;
+  const int sub = threadIdx.x % LP;
+  const int64_t rr = row < rows ? row : rows - 1;
+  float acc = 0.f;
+  const int64_t e0 = rr * D + sub * 8;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = ta == kF32 ? static_cast<const float*>(a)[e0 + e]
+                               : static_cast<float>(static_cast<const bf16*>(a)[e0 + e]);
+    const float y = tb == kF32 ? static_cast<const float*>(bp)[e0 + e]
+                               : static_cast<float>(static_cast<const bf16*>(bp)[e0 + e]);
+    acc = fmaf(x, y, acc);
+  }
+#pragma unroll
+  for (int off = LP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LP);
+  if (sub == 0 && row < rows) out[row] = acc;
+}
+
+}  // namespace
+
+bool bwd_supported(const GroupedArgs& g) {
+  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L >= 1 &&
+         (static_cast<int64_t>(g.L) + FBN) * g.row_stride * g.D * 4 < (int64_t{1} << 31);
+}
+
+hipError_t launch_bwd(const BwdArgs& b, hipStream_t s) {
+  const GroupedArgs& g = b.g;
+  if (!bwd_supported(g) || !b.go || !b.lse || !b.delta || !b.dq || !b.dk || !b.dv) return hipErrorInvalidValue;
+  const int tiles = (g.L + FBM - 1) / FBM;
+  const int64_t nwg = static_cast<int64_t>(tiles) * g.problems * g.heads;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const unsigned grid = static_cast<unsigned>(nwg);
+  if (g.D == 128) {
+    hipLaunchKernelGGL(bwd_dq_kernel<128>, dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, 0>), dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<128, 1>), dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
+  } else {
+    hipLaunchKernelGGL(bwd_dq_kernel<64>, dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, 0>), dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
+    hipLaunchKernelGGL((bwd_dkdv_kernel<64, 1>), dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rowdot(const void* a, ElemType ta, const void* bp, ElemType tb, float* out, int64_t rows, int D,
+                         hipStream_t s) {
+  if (rows <= 0 || (D != 64 && D != 128)) return hipErrorInvalidValue;
+  const int64_t threads = rows * (D / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (D == 128)
+    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a, ta, bp, tb, out,
+                       rows);
+  else
+    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a, ta, bp, tb, out,
+                       rows);
+  return hipGetLastError();
+}
+
+}  // namespace monarch

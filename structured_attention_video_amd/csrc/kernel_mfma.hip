@@ -20,141 +20,12 @@
 // Scores never leave the chip and memory stays linear in N, the "SRAM
 // reduction" design the MonarchRT pages describe for their kernels
 // (gist.science explainer, section 2.C).
-#include "mfma_common.h"
+#include "flash_common.h"
 
 namespace monarch {
 namespace {
 
 using namespace mfma;
-
-constexpr float kRescaleThreshold = 8.0f;
-
-__device__ __forceinline__ int64_t problem_base(const GroupedArgs& a, int p) {
-  return static_cast<int64_t>(p / a.inner) * a.outer + (p % a.inner);
-}
-
-// Map the hardware workgroup id to a logical id so that consecutive logical
-// ids run on the same XCD (workgroups are dealt to the 8 XCDs round-robin).
-__device__ __forceinline__ int xcd_order(int w, int nwg) {
-  const int q = nwg >> 3, r = nwg & 7, x = w & 7, slot = w >> 3;
-  return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
-}
-
-// Per-thread byte offsets of the 16-byte chunks a cooperative tile load
-// covers: chunk id = tid + NT*c -> row id/CPR, channels 8*(id%CPR).. (16
-// consecutive lanes read one 256-byte row).
-template <int D, int ROWS, int NT>
-struct TileOffsets {
-  static constexpr int CPR = D / 8;
-  static constexpr int N = ROWS * CPR / NT;
-  uint32_t g[N];  // global, relative to row 0 of the tile
-  uint32_t s[N];  // LDS
-  __device__ __forceinline__ TileOffsets(int tid, int64_t rs) {
-#pragma unroll
-    for (int c = 0; c < N; ++c) {
-      const int id = tid + NT * c;
-      g[c] = static_cast<uint32_t>(((id / CPR) * rs * D + (id % CPR) * 8) * 2);
-      s[c] = static_cast<uint32_t>((id / CPR) * KRow<D>::bytes + (id % CPR) * 16);
-    }
-  }
-  __device__ __forceinline__ void load(u32x4* r, __amdgpu_buffer_rsrc_t src, uint32_t tile_off) const {
-#pragma unroll
-    for (int c = 0; c < N; ++c) r[c] = bload16(src, g[c] + tile_off);
-  }
-  __device__ __forceinline__ void store(char* lds, const u32x4* r) const {
-#pragma unroll
-    for (int c = 0; c < N; ++c) *reinterpret_cast<u32x4*>(lds + s[c]) = r[c];
-  }
-};
-
-// ---------------------------------------------------------------- flash
-constexpr int FBM = 128;  // query rows per workgroup
-constexpr int FBN = 64;   // keys per LDS tile
-constexpr int FNT = 256;  // threads
-
-// LDS tiles of the flash kernel: 64 rows x D channels, rows unpadded, the
-// 16-byte chunks of row r permuted by c -> c ^ swz(r). Tiles are filled by
-// buffer loads that write LDS directly (64 lanes x 16 bytes = one contiguous
-// kilobyte per instruction; lane i fetches the global chunk that belongs in
-// slot i). The swizzle keeps every 16-lane phase of the 16-byte K reads and
-// of the transposing V reads on distinct banks.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((2 * r) & 15) | ((r >> 3) & 1);
-  else return (2 * ((r >> 1) & 3)) | ((r >> 3) & 1);
-}
-
-template <int D>
-struct SwTile {
-  static constexpr int ROWB = D * 2;          // bytes per row
-  static constexpr int CPR = D / 8;           // 16-byte chunks per row
-  static constexpr int bytes = FBN * ROWB;    // one tile
-  static constexpr int RPI = 1024 / ROWB;     // rows per load instruction
-  static constexpr int IPW = FBN / 4 / RPI;   // load instructions per wave per tile
-  static constexpr int total = 4 * bytes;     // two-slot rings for K and V
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from a buffer straight into LDS (lane i -> lds + 16*i).
-// Only the device pass sees the builtin: instantiating it in the host pass
-// silently drops the host launch stub of the kernel that uses it, and device
-// functions never run on the host.
-template <int POLICY = 0>
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t src, char* lds, uint32_t voff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds, 16, voff, 0, 0, POLICY);
-#else
-  (void)src; (void)lds; (void)voff;
-#endif
-}
-
-
-// Per-lane byte offsets: DMA source chunks (tile 0) and LDS read addresses.
-template <int D>
-struct FlashOffsets {
-  using T = SwTile<D>;
-  uint32_t src_off[T::IPW];  // global, relative to the tile's first row
-  uint32_t k[D / 16];     // K read, k-step ks, rows 0..31 (+32 rows = +32*ROWB)
-  uint32_t v[D / 32][2];  // V^T reads, channel tile mt, keys +0..3 / +8..11 (+16*step rows)
-  __device__ __forceinline__ FlashOffsets(int wave, int lane, int64_t rs) {
-#pragma unroll
-    for (int i = 0; i < T::IPW; ++i) {
-      const int row = 16 * wave + T::RPI * i + lane / T::CPR;
-      const int c = (lane % T::CPR) ^ swz<D>(row);
-      src_off[i] = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
-    }
-    const int r = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) k[ks] = r * T::ROWB + 16 * ((2 * ks + h) ^ swz<D>(r));
-    const int j = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int sec = 0; sec < 2; ++sec) {
-        const int row = 4 * (g >> 1) + (j >> 2) + 8 * sec;
-        const int ch = 32 * mt + 16 * (g & 1) + 4 * (j & 3);
-        v[mt][sec] = row * T::ROWB + 16 * ((ch / 8) ^ swz<D>(row)) + (ch % 8) * 2;
-      }
-  }
-  // Issue this wave's share (16 rows) of one tile's global -> LDS copy.
-  __device__ __forceinline__ void dma(char* tile, __amdgpu_buffer_rsrc_t src, uint32_t tile_off, int wave) const {
-#pragma unroll
-    for (int i = 0; i < T::IPW; ++i)
-      lds_dma16(src, tile + (16 * wave + T::RPI * i) * T::ROWB, src_off[i] + tile_off);
-  }
-};
-
-// wait for this wave's outstanding global -> LDS copies
-__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
-
-__device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int nvalid, int h) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      if (32 * t + acc_key(i, h) >= nvalid) s[t][i] = -INFINITY;
-}
 
 // Running max update with lazy rescale of the accumulator.
 template <int D>
@@ -173,20 +44,6 @@ __device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D /
   }
 }
 
-template <int D>
-__device__ __forceinline__ bf16x8 k_operand(const char* kl, const FlashOffsets<D>& fo, int ks, int t) {
-  return ld_bf16x8(kl + fo.k[ks] + t * 32 * SwTile<D>::ROWB);
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8 v_operand(const char* vl, const FlashOffsets<D>& fo, int mt, int st) {
-  const char* base = vl + st * 16 * SwTile<D>::ROWB;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + fo.v[mt][0]));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + fo.v[mt][1]));
-  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-// S^T for a 64-key tile (two independent 32-key accumulator chains)
 template <int D>
 __device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const FlashOffsets<D>& fo,
                                          const bf16x8 (&qf)[D / 16]) {
@@ -384,8 +241,10 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   probs(st.s, pb, st.l, c, st.m);
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
-  const float inv = 1.f / halves_sum(st.l);  // both lane halves of a row are active together
-  store_out<D, OUT_F32, POLICY>(ro, row0 + (lane & 31), rs, st.o, inv, lane);
+  const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
+  if (a.lse && h == 0 && row0 + (lane & 31) < L)
+    a.lse[hd * (a.head_elems / D) + base + (row0 + (lane & 31)) * rs] = st.m + __builtin_amdgcn_logf(lsum);
+  store_out<D, OUT_F32, POLICY>(ro, row0 + (lane & 31), rs, st.o, 1.f / lsum, lane);
 }
 
 template <int D, bool OUT_F32>
@@ -509,7 +368,9 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(Grouped
       o[mt] = mma(__builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7)), pb, o[mt]);
     }
   }
-  const float inv = 1.f / halves_sum(l);
+  const float lsum = halves_sum(l);
+  const float inv = 1.f / lsum;
+  if (a.lse && h == 0 && r < L) a.lse[hd * (a.head_elems / D) + base + r * rs] = mx + __builtin_amdgcn_logf(lsum);
   if constexpr (OUT_F32) {
     store_out<D, true>(ro, r, rs, o, inv, lane);
   } else {

@@ -127,6 +127,7 @@ __global__ void __launch_bounds__(256) tiny_kernel(GroupedArgs a, int64_t total)
 #pragma unroll
     for (int e = 0; e < 8; ++e) o[e] *= inv;
     if (ok) store8(a.o, row, o, a.o_type);
+    if (ok && a.lse && sub == 0) a.lse[hd * (a.head_elems / D) + base + i * a.row_stride] = mx + __builtin_amdgcn_logf(sum);
   }
 }
 

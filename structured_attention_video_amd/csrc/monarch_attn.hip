@@ -32,6 +32,30 @@ ElemType as_elem(int32_t dt) { return dt == MONARCH_FP32 ? kF32 : kBF16; }
 // The fused control block follows Y in the workspace, 256-byte aligned.
 int64_t ctl_offset(const monarch_plan_info& p) { return (tensor_bytes(p, p.y_dtype) + 255) / 256 * 256; }
 
+int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Backward workspace: Y and dY (bf16), the stage-2 partial dQ and dK (fp32),
+// then per-row lse and delta of both stages (fp32), each section 256-aligned.
+struct BwdLayout {
+  int64_t y, dy, dq2, dk2, lse1, lse2, del1, del2, total;
+};
+BwdLayout bwd_layout(const monarch_plan_info& p) {
+  const int64_t t2 = tensor_bytes(p, MONARCH_BF16), t4 = tensor_bytes(p, MONARCH_FP32);
+  const int64_t rows = align256(p.batch * p.heads * p.N * 4);
+  BwdLayout l{};
+  l.y = 0;
+  l.dy = align256(t2);
+  l.dq2 = l.dy + align256(t2);
+  l.dk2 = l.dq2 + align256(t4);
+  l.lse1 = l.dk2 + align256(t4);
+  l.lse2 = l.lse1 + rows;
+  l.del1 = l.lse2 + rows;
+  l.del2 = l.del1 + rows;
+  l.total = l.del2 + rows;
+  return l;
+}
+
+
 // Grouped-attention description of stage 1 (contiguous blocks of b tokens).
 GroupedArgs stage1_args(const monarch_plan_info& p, const void* q, const void* k, const void* v,
                         void* out, int32_t out_dtype) {
@@ -88,6 +112,20 @@ hipError_t launch(int32_t kernel, const GroupedArgs& a, hipStream_t s) {
     case kKernelTiny: return launch_tiny(a, s);
     default: return launch_generic(a, s);
   }
+}
+
+bool bwd_plan_ok(const monarch_plan_info& p) {
+  if (p.dtype != MONARCH_BF16 || (p.flags & MONARCH_FLAG_GENERIC)) return false;
+  const bool has1 = p.b > 1, has2 = p.m_tau > 1;
+  if (has1 || !has2) {
+    GroupedArgs a = stage1_args(p, nullptr, nullptr, nullptr, nullptr, MONARCH_BF16);
+    if (!bwd_supported(a) || choose_kernel(a, p.flags) == kKernelGeneric) return false;
+  }
+  if (has2) {
+    GroupedArgs a = stage2_args(p, nullptr, nullptr, nullptr, MONARCH_BF16, nullptr);
+    if (!bwd_supported(a) || choose_kernel(a, p.flags) == kKernelGeneric) return false;
+  }
+  return true;
 }
 
 // bit-level test, independent of floating-point compile flags
@@ -268,6 +306,107 @@ monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, cons
   const int64_t io = tensor_bytes(p, p.dtype), ny = tensor_bytes(p, ydt);
   if (overlap(o, io, q, io) || overlap(o, io, k, io) || overlap(o, io, y, ny)) return MONARCH_ERR_ALIAS;
   return run_stage2(p, q, k, y, ydt, o, static_cast<hipStream_t>(stream));
+}
+
+size_t monarch_attn_backward_workspace_size(const monarch_plan* plan) {
+  if (!plan || !bwd_plan_ok(plan->info)) return 0;
+  return static_cast<size_t>(bwd_layout(plan->info).total);
+}
+
+monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                     const void* o, const void* grad_o, void* grad_q, void* grad_k, void* grad_v,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !o || !grad_o || !grad_q || !grad_k || !grad_v || !workspace)
+    return MONARCH_ERR_INVALID_ARG;
+  const monarch_plan_info& p = plan->info;
+  if (!bwd_plan_ok(p)) return MONARCH_ERR_UNSUPPORTED;
+  const void* ins[] = {q, k, v, o, grad_o};
+  void* outs[] = {grad_q, grad_k, grad_v};
+  for (const void* x : ins)
+    if (misaligned(x)) return MONARCH_ERR_UNALIGNED;
+  for (const void* x : outs)
+    if (misaligned(x)) return MONARCH_ERR_UNALIGNED;
+  if (misaligned(workspace)) return MONARCH_ERR_UNALIGNED;
+  const BwdLayout lay = bwd_layout(p);
+  if (static_cast<int64_t>(workspace_bytes) < lay.total) return MONARCH_ERR_WORKSPACE;
+  const int64_t io = tensor_bytes(p, p.dtype);
+  for (int i = 0; i < 3; ++i) {
+    if (overlap(outs[i], io, workspace, lay.total)) return MONARCH_ERR_ALIAS;
+    for (const void* x : ins)
+      if (overlap(outs[i], io, x, io)) return MONARCH_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlap(outs[i], io, outs[j], io)) return MONARCH_ERR_ALIAS;
+  }
+  for (const void* x : ins)
+    if (overlap(workspace, lay.total, x, io)) return MONARCH_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  void* y = w + lay.y;
+  void* dy = w + lay.dy;
+  float* dq2 = reinterpret_cast<float*>(w + lay.dq2);
+  float* dk2 = reinterpret_cast<float*>(w + lay.dk2);
+  float* lse1 = reinterpret_cast<float*>(w + lay.lse1);
+  float* lse2 = reinterpret_cast<float*>(w + lay.lse2);
+  float* del1 = reinterpret_cast<float*>(w + lay.del1);
+  float* del2 = reinterpret_cast<float*>(w + lay.del2);
+  const int64_t rows = p.batch * p.heads * p.N;
+  const int D = static_cast<int>(p.head_dim);
+  const bool has1 = p.b > 1, has2 = p.m_tau > 1;
+  auto ok = [](hipError_t e) { return e == hipSuccess; };
+
+  // forward again, keeping Y and the per-row statistics
+  GroupedArgs f1{}, f2{};
+  if (has1 || !has2) {
+    f1 = stage1_args(p, q, k, v, y, MONARCH_BF16);
+    f1.lse = lse1;
+    if (!ok(launch(choose_kernel(f1, p.flags), f1, s))) return MONARCH_ERR_HIP;
+  }
+  if (has2) {
+    // values: Y (or V when stage 1 is the identity). The recomputed output is
+    // kept in fp32 (in the dQ2 section, free until the stage-2 backward): delta
+    // = rowsum(G * O) then uses O before its bf16 rounding, which matters
+    // because dS = P * (dP - delta) subtracts two nearly equal numbers.
+    f2 = stage2_args(p, q, k, has1 ? y : v, MONARCH_BF16, dq2);
+    f2.o_type = kF32;
+    f2.lse = lse2;
+    if (!ok(launch(choose_kernel(f2, p.flags), f2, s))) return MONARCH_ERR_HIP;
+  }
+  if (has2) {
+    BwdArgs b2{};
+    b2.g = f2;
+    b2.go = grad_o;
+    b2.lse = lse2;
+    b2.delta = del2;
+    if (!ok(launch_rowdot(grad_o, kBF16, dq2, kF32, del2, rows, D, s))) return MONARCH_ERR_HIP;
+    if (has1) {  // partial dQ, dK in fp32; dY (bf16) feeds stage 1
+      b2.dq = dq2; b2.dq_type = kF32;
+      b2.dk = dk2; b2.dk_type = kF32;
+      b2.dv = dy; b2.dv_type = kBF16;
+    } else {     // stage 2 alone: final gradients
+      b2.dq = grad_q; b2.dq_type = kBF16;
+      b2.dk = grad_k; b2.dk_type = kBF16;
+      b2.dv = grad_v; b2.dv_type = kBF16;
+    }
+    if (!ok(launch_bwd(b2, s))) return MONARCH_ERR_HIP;
+  }
+  if (has1 || !has2) {
+    BwdArgs b1{};
+    b1.g = f1;
+    b1.go = has2 ? dy : grad_o;
+    b1.lse = lse1;
+    b1.delta = del1;
+    if (!ok(launch_rowdot(b1.go, kBF16, has2 ? y : o, kBF16, del1, rows, D, s))) return MONARCH_ERR_HIP;
+    b1.dq = grad_q; b1.dq_type = kBF16;
+    b1.dk = grad_k; b1.dk_type = kBF16;
+    b1.dv = grad_v; b1.dv_type = kBF16;
+    if (has2) {
+      b1.dq_in = dq2;
+      b1.dk_in = dk2;
+    }
+    if (!ok(launch_bwd(b1, s))) return MONARCH_ERR_HIP;
+  }
+  return MONARCH_OK;
 }
 
 const char* monarch_status_string(monarch_status status) {

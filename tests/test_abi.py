@@ -225,3 +225,39 @@ def test_fused_flag_ignored_where_it_does_not_apply(kw):
     assert info.fused == 0
     plain, ws_plain = _info(flags=flags & ~_lib.FLAG_FUSED, **kw)
     assert ws == ws_plain
+
+
+# ------------------------------------------------------------------ backward
+def test_backward_workspace_size():
+    st, h = _plan(heads=12, grid=(21, 30, 52))
+    n = L.monarch_attn_backward_workspace_size(h)
+    rows = 12 * 32760 * 4
+    t2, t4 = 12 * 32760 * 128 * 2, 12 * 32760 * 128 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    assert n == 2 * up(t2) + 2 * up(t4) + 4 * up(rows)
+    L.monarch_attn_destroy(h)
+    for kw in (dict(dtype=1), dict(flags=_lib.FLAG_GENERIC)):
+        st, h = _plan(**kw)
+        assert st == _lib.OK and L.monarch_attn_backward_workspace_size(h) == 0
+        L.monarch_attn_destroy(h)
+
+
+def test_backward_argument_errors():
+    F = 1 << 36  # fake, 16-byte aligned device addresses, never dereferenced
+    st, h = _plan(heads=2, grid=(4, 6, 10))
+    n = L.monarch_attn_backward_workspace_size(h)
+    io = 2 * 240 * 128 * 2
+    ptr = [F + i * (1 << 30) for i in range(9)]
+    ws = F + 20 * (1 << 30)
+    call = lambda p, wsz=n, w=ws: L.monarch_attn_backward(h, *p, w, wsz, None)
+    assert call([0] + ptr[1:8]) == _lib.ERR_INVALID_ARG
+    assert call(ptr[:8], w=0) == _lib.ERR_INVALID_ARG
+    assert call(ptr[:8], wsz=n - 1) == _lib.ERR_WORKSPACE
+    assert call([ptr[0] + 4] + ptr[1:8]) == _lib.ERR_UNALIGNED
+    assert call(ptr[:5] + [ptr[0] + 64] + ptr[6:8]) == _lib.ERR_ALIAS        # grad_q overlaps q
+    assert call(ptr[:6] + [ptr[5] + io - 16, ptr[7]]) == _lib.ERR_ALIAS       # grad_k overlaps grad_q
+    assert call(ptr[:8], w=ptr[7] + 32) == _lib.ERR_ALIAS                      # workspace overlaps grad_v
+    L.monarch_attn_destroy(h)
+    st, h = _plan(heads=2, grid=(4, 6, 10), dtype=1)
+    assert L.monarch_attn_backward(h, *ptr[:8], ws, 1 << 30, None) == _lib.ERR_UNSUPPORTED
+    L.monarch_attn_destroy(h)

@@ -1,0 +1,91 @@
+"""GPU parity of the backward pass (dQ, dK, dV through both stages) against
+the fp64 backward oracle, which is itself pinned by finite differences and
+autograd (test_oracle_backward_pins.py).
+
+Tolerance (bf16 inputs; Y, dY, P and dS enter matrix products in bf16, all
+sums in fp32): per gradient tensor, rel-L2 <= 1e-2 (norms below 1e-3 per
+element count as 1e-3) and max-abs <= 3e-2 times max(1, max |reference|) -
+the forward's bar, relative to the gradient's scale.
+"""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from structured_attention_video_amd import MonarchPlan
+from gpu_util import say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16 = torch.bfloat16
+
+
+def check(got, want, what):
+    got, want = np.asarray(got, np.float64), np.asarray(want, np.float64)
+    # (a gradient that is exactly zero, e.g. dQ with a single key, is measured
+    # against an absolute floor instead of its own norm)
+    rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-3 * np.sqrt(want.size))
+    mx = np.abs(got - want).max()
+    bound = 3e-2 * max(1.0, np.abs(want).max())
+    say(f"  {what}: rel-L2 {rel:.2e}, max-abs {mx:.2e} (bound {bound:.2e})")
+    assert np.isfinite(got).all(), what
+    assert rel <= 1e-2 and mx <= bound, f"{what}: rel-L2 {rel:.3e} max-abs {mx:.3e}"
+
+
+def grads(q, k, v, g, grid, align="frame", tile=0, custom_b=0):
+    B, Hh, N, d = q.shape
+    plan = MonarchPlan(B, Hh, d, grid, align=align, tile_tokens=tile, custom_b=custom_b, dtype=q.dtype,
+                       allow_unaligned=(align == "custom"))
+    say(f"  plan b={plan.info['b']} m_tau={plan.info['m_tau']} ws={plan.backward_workspace_bytes}")
+    qd, kd, vd, gd = (x.to(DEV) for x in (q, k, v, g))
+    o = plan.forward(qd, kd, vd)
+    dq, dk, dv = plan.backward(qd, kd, vd, o, gd)
+    torch.cuda.synchronize()
+    return [to_np(x) for x in (dq, dk, dv)], plan, (qd, kd, vd, o, gd)
+
+
+SMALL = [
+    # (grid, d, align, tile, custom_b)
+    ((3, 5, 20), 128, "frame", 0, 0),    # b=100 (group kernel forward), m=3 (tiny kernel forward)
+    ((5, 4, 37), 128, "frame", 0, 0),    # b=148: two key tiles with a ragged tail, m=5
+    ((5, 4, 37), 128, "row", 0, 0),      # b=37, m=20
+    ((6, 7, 13), 64, "frame", 0, 0),     # d=64
+    ((6, 7, 13), 64, "row", 0, 0),
+    ((9, 4, 25), 128, "frame", 300, 0),  # tiled: m_tau=3, 3 tiles
+    ((10, 15, 8), 128, "row", 0, 0),     # m=150 > 128: stage 2 over several tiles
+    ((2, 9, 33), 128, "frame", 0, 0),    # m=2, b=297
+    ((3, 5, 20), 128, "dense", 0, 0),    # b=N: one stage
+    ((3, 5, 20), 128, "token", 0, 0),    # b=1: stage 2 alone
+    ((4, 6, 10), 128, "custom", 0, 20),  # unaligned split
+    ((1, 1, 1), 128, "dense", 0, 0),     # one token
+]
+
+
+@pytest.mark.parametrize("grid,d,align,tile,cb", SMALL,
+                         ids=[f"{g[0]}x{g[1]}x{g[2]}-d{d}-{a}-t{t}" for g, d, a, t, cb in SMALL])
+def test_backward_small_cases(grid, d, align, tile, cb):
+    q, k, v = datagen.qkv(2, 3, grid, d, (51, 52, 53), dtype=BF16)
+    g = datagen.qkv(2, 3, grid, d, (54, 55, 56), dtype=BF16)[0]
+    got, _, _ = grads(q, k, v, g, grid, align, tile, cb)
+    b = oracle.block_size(grid, align, cb)
+    want = oracle.monarch_backward(q, k, v, g, b, tile or None)
+    for name, x, y in zip(("dQ", "dK", "dV"), got, want):
+        check(x, y, f"{grid} {align} t{tile} {name}")
+
+
+@pytest.mark.parametrize("name", ["frame_bf16", "row_bf16", "tiled_bf16"])
+def test_backward_full_size_two_heads(name):
+    c = datagen.CONFIGS[name]
+    q, k, v = datagen.config_inputs(name, heads=2)
+    g = datagen.qkv(1, 2, c["grid"], 128, (61, 62, 63), dtype=BF16)[0]
+    got, plan, args = grads(q, k, v, g, c["grid"], c["align"], c["tile_tokens"])
+    b = oracle.block_size(c["grid"], c["align"])
+    want = oracle.monarch_backward(q, k, v, g, b, c["tile_tokens"])
+    for nm, x, y in zip(("dQ", "dK", "dV"), got, want):
+        check(x, y, f"{name} {nm}")
+    # deterministic: no atomics anywhere
+    again = plan.backward(*args)
+    torch.cuda.synchronize()
+    for x, y in zip(got, again):
+        assert np.array_equal(x, to_np(y))
