@@ -13,7 +13,8 @@ Prints ONE JSON line. Besides the contract fields it carries:
   stages_two_launch  per-stage ms and rates of the two-launch path (stage 1
                 then stage 2), timed separately; dense: the library's own
                 dense softmax-attention kernel at the same shape; backward:
-                the gradient pass at the same shape.
+                the gradient pass at the same shape; chunk: one frame-causal
+                chunk of three frames after a cache of the earlier frames.
 A call is stage 1 then stage 2 (two launches); --fused auto/on times the
 library's one-launch fused variant instead where it applies (frame and tiled
 alignments). call_ms_events: per-call device time from HIP events in a second
@@ -307,6 +308,19 @@ def main():
         out["backward"] = {"ms_per_call_p50": round(pct(tb, 0.5), 4),
                            "tflops_at_2p5x_forward": round(2.5 * flops / (pct(tb, 0.5) * 1e-3) / 1e12, 2)}
         del bws, go, gq, gk, gv, ob
+
+    # one frame-causal chunk (the last three frames against the cache of all earlier
+    # frames: autoregressive generation, three frames per chunk) at the same shape
+    T = c["grid"][0]
+    if info["tiles"] == 1 and info["m_tau"] > 1 and T >= 4 and (c["grid"][1] * c["grid"][2]) % info["b"] == 0:
+        yc = torch.zeros(q.shape, dtype=split.y_dtype, device=dev) if info["b"] > 1 else None
+        oc = torch.empty_like(q)
+        split.chunk_forward(q, k, v, yc, oc, 0, T - 3)
+        for _ in range(2):
+            split.chunk_forward(q, k, v, yc, oc, T - 3, T)
+        tc = timed(lambda: split.chunk_forward(q, k, v, yc, oc, T - 3, T), args.steps)
+        out["chunk"] = {"frames": [T - 3, T], "cached_frames": T - 3, "ms_per_call_p50": round(pct(tc, 0.5), 4)}
+        del yc, oc
 
     if not args.no_dense:
         dplan = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align="dense", dtype=dt)

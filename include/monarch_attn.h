@@ -153,6 +153,22 @@ monarch_status monarch_attn_stage1(const monarch_plan* plan, const void* q, cons
 monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, const void* k,
                                    const void* y, void* o, void* stream);
 
+/* One chunk of frame-causal (autoregressive) generation: the forward for the frames
+ * t0 .. t1-1 of the plan's video, where every query of the chunk sees the keys of all frames
+ * before t1 (earlier chunks and the whole current chunk) - the block-causal regime of
+ * autoregressive video generation the pages target (Self-Forcing, abstract). The pages give no
+ * formula for it; the reading used here: stage 1 is unchanged (its blocks lie inside frames), and
+ * each stage-2 group keeps its rows of frames < t1 as keys and values and its rows of frames
+ * t0 .. t1-1 as queries. With t0 = 0, t1 = T it is the ordinary forward.
+ *   q, k, v, o, y: [batch, heads, N, head_dim] arrays over the whole video (plan dtype; y: the
+ *   plan's y_dtype). Read: q and v of frames t0..t1-1, k of frames 0..t1-1, y of frames 0..t0-1
+ *   (the stage-1 outputs of earlier chunks, i.e. this call's y from earlier calls). Written: y and
+ *   o of frames t0..t1-1; nothing else. y may be NULL when b = 1 (stage 1 is the identity).
+ * Supported for untiled plans whose blocks lie inside frames (b divides H*W) with m_tau > 1;
+ * else MONARCH_ERR_UNSUPPORTED. Asynchronous on `stream`. */
+monarch_status monarch_attn_chunk_forward(const monarch_plan* plan, int32_t t0, int32_t t1, const void* q,
+                                          const void* k, const void* v, void* y, void* o, void* stream);
+
 /* Bytes of device workspace monarch_attn_backward needs (0 when the plan has no backward:
  * fp32 plans and MONARCH_FLAG_GENERIC plans). Independent of the forward's workspace. */
 size_t monarch_attn_backward_workspace_size(const monarch_plan* plan);

@@ -62,6 +62,8 @@ __all__ = [
     "monarch_matrix",
     "monarch_bruteforce",
     "dense_attention",
+    "monarch_chunk_forward",
+    "monarch_chunk_bruteforce",
     "flop_count",
 ]
 
@@ -318,3 +320,62 @@ def dense_attention(q, k, v, scale: Optional[float] = None,
         else:
             out[c0:c0 + len(r)] = softmax_rows(s * (q[r] @ k.T)) @ v
     return out
+
+
+def monarch_chunk_forward(q, k, v, b: int, frame_tokens: int, t0: int, t1: int,
+                          scale: Optional[float] = None) -> np.ndarray:
+    """One chunk of frame-causal generation: O for the frames t0..t1-1.
+
+    The reading (the pages target autoregressive, chunk-by-chunk generation
+    with Self-Forcing but give no formula for it): stage 1 is unchanged, its
+    blocks lie inside frames; each stage-2 group keeps its rows of frames
+    before t1 as keys and values and its rows of frames t0..t1-1 as queries.
+    Inputs [..., N, d] over the whole video (untiled); rows of frames >= t1
+    are never used. Returns O rows of the chunk, [..., (t1-t0)*frame_tokens, d].
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    *lead, N, d = q.shape
+    check_plan(N, b, N)
+    assert frame_tokens % b == 0 and N % frame_tokens == 0 and 0 <= t0 < t1 <= N // frame_tokens
+    s = _scale(d, scale)
+    bpf = frame_tokens // b
+    r0, r1 = t0 * bpf, t1 * bpf  # block rows of the chunk, keys: blocks 0..r1-1
+    qf, kf, vf = q.reshape(-1, N, d), k.reshape(-1, N, d), v.reshape(-1, N, d)
+    out = np.empty((qf.shape[0], (r1 - r0) * b, d))
+    for h in range(qf.shape[0]):
+        n_keys = r1 * b  # tokens of frames 0..t1-1
+        y = stage1(qf[h, :n_keys], kf[h, :n_keys], vf[h, :n_keys], b, s)  # [r1*b, d]
+        qg = qf[h, :n_keys].reshape(r1, b, d).transpose(1, 0, 2)  # [b groups, r1 rows, d]
+        kg = kf[h, :n_keys].reshape(r1, b, d).transpose(1, 0, 2)
+        yg = y.reshape(r1, b, d).transpose(1, 0, 2)
+        p2 = softmax_rows(s * np.matmul(qg[:, r0:r1], kg.transpose(0, 2, 1)))  # [b, r1-r0, r1]
+        out[h] = np.matmul(p2, yg).transpose(1, 0, 2).reshape(-1, d)
+    return out.reshape(*lead, (r1 - r0) * b, d)
+
+
+def monarch_chunk_bruteforce(q, k, v, b: int, frame_tokens: int, t0: int, t1: int,
+                             scale: Optional[float] = None) -> np.ndarray:
+    """The chunk output by explicit loops over tokens (tiny inputs): for a
+    query in block i (at in-block position j) of the chunk,
+    O = sum_{i' < r1} P2[i, i'] * sum_j'' P1_{i'}[j, j''] * V[i' * b + j''],
+    P2 normalised over the blocks i' < r1 only. q, k, v: [N, d]."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    N, d = q.shape
+    s = _scale(d, scale)
+    bpf = frame_tokens // b
+    r0, r1 = t0 * bpf, t1 * bpf
+    out = np.zeros(((r1 - r0) * b, d))
+    for i in range(r0, r1):
+        for j in range(b):
+            n = i * b + j
+            z2 = [s * float(np.dot(q[n], k[ip * b + j])) for ip in range(r1)]
+            w2 = [math.exp(x - max(z2)) for x in z2]
+            for ip in range(r1):
+                p2 = w2[ip] / sum(w2)
+                m = ip * b + j
+                z1 = [s * float(np.dot(q[m], k[ip * b + jj])) for jj in range(b)]
+                w1 = [math.exp(x - max(z1)) for x in z1]
+                for jj in range(b):
+                    out[n - r0 * b] += p2 * w1[jj] / sum(w1) * v[ip * b + jj]
+    return out
+

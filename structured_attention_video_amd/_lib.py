@@ -33,6 +33,7 @@ EXPORTED = [
     "monarch_attn_plan_info", "monarch_attn_forward", "monarch_attn_stage1",
     "monarch_attn_stage2", "monarch_status_string", "monarch_attn_kernel_name",
     "monarch_attn_abi_version", "monarch_attn_backward_workspace_size", "monarch_attn_backward",
+    "monarch_attn_chunk_forward",
 ]
 
 
@@ -91,5 +92,7 @@ def lib() -> ctypes.CDLL:
     L.monarch_attn_backward_workspace_size.restype = sz
     L.monarch_attn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.monarch_attn_backward.restype = i32
+    L.monarch_attn_chunk_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp]
+    L.monarch_attn_chunk_forward.restype = i32
     _lib = L
     return L

@@ -147,6 +147,21 @@ class MonarchPlan:
         _check(st, "monarch_attn_stage2")
         return out
 
+    def chunk_forward(self, q, k, v, y, out, t0: int, t1: int):
+        """Frames t0..t1-1 of frame-causal generation (see monarch_attn_chunk_forward).
+
+        All tensors cover the whole video: reads q, v of the chunk, k of frames < t1
+        and y (the stage-1 cache) of frames < t0; writes y and out of the chunk."""
+        self._check_io(q, k, v, out)
+        if y is not None:
+            if tuple(y.shape) != self.shape or not y.is_contiguous() or y.dtype != self.y_dtype or not y.is_cuda:
+                raise ValueError("y must be a contiguous GPU tensor of the plan's shape and Y dtype")
+        st = _lib.lib().monarch_attn_chunk_forward(self._h, int(t0), int(t1), q.data_ptr(), k.data_ptr(),
+                                                   v.data_ptr(), y.data_ptr() if y is not None else None,
+                                                   out.data_ptr(), self._stream(q))
+        _check(st, "monarch_attn_chunk_forward")
+        return out
+
     @property
     def backward_workspace_bytes(self) -> int:
         """Workspace bytes of backward() (0: this plan has no backward)."""

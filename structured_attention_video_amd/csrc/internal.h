@@ -28,7 +28,10 @@ struct GroupedArgs {
   int32_t inner;
   int64_t outer;
   int64_t row_stride; // in tokens
-  int32_t L;          // rows per problem
+  int32_t L;          // rows per problem (keys and values: rows 0..L-1)
+  int32_t q_row0;     // first query row inside each problem (0 when every row queries)
+  int32_t Lq;         // query rows per problem, q_row0 + Lq <= L (L when every row queries);
+                      // outputs (and lse) are written for the query rows only
   int32_t D;          // head dim
   float scale_log2;   // softmax scale * log2(e)
   ElemType qk_type;

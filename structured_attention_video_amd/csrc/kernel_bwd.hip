@@ -316,7 +316,8 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const void* a, int ta, cons
 }  // namespace
 
 bool bwd_supported(const GroupedArgs& g) {
-  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L >= 1 &&
+  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L >= 1 && g.q_row0 == 0 &&
+         g.Lq == g.L &&
          (static_cast<int64_t>(g.L) + FBN) * g.row_stride * g.D * 4 < (int64_t{1} << 31);
 }
 

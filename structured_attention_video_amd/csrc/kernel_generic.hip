@@ -49,8 +49,9 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
 
   const int tid = threadIdx.x;
   const int part = tid % SPLIT;
-  const int row = chunk * rows_per_wg + tid / SPLIT;
-  const bool row_ok = (tid / SPLIT) < rows_per_wg && row < a.L;
+  const int qr0 = chunk * rows_per_wg + tid / SPLIT;  // within the query rows
+  const int row = a.q_row0 + qr0;
+  const bool row_ok = (tid / SPLIT) < rows_per_wg && qr0 < a.Lq;
 
   float qr[PART];
   float acc[PART];
@@ -116,10 +117,10 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
 hipError_t launch_generic(const GroupedArgs& a, hipStream_t stream) {
   const int split = a.D / PART;
   int threads = 256;
-  const int need = a.L * split;
+  const int need = a.Lq * split;
   if (need < threads) threads = ((need + 63) / 64) * 64;
   const int rows_per_wg = threads / split;
-  const int chunks = (a.L + rows_per_wg - 1) / rows_per_wg;
+  const int chunks = (a.Lq + rows_per_wg - 1) / rows_per_wg;
   const int64_t grid = static_cast<int64_t>(chunks) * a.problems * a.heads;
   if (grid <= 0 || grid > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.D == 64)

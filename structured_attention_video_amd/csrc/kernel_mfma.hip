@@ -161,15 +161,18 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   const int64_t base = problem_base(a, p);
   const int64_t rs = a.row_stride;
   const int L = a.L;
-  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  // query rows: q_row0 .. q_row0 + Lq - 1 of the problem (qbase is the first)
+  const int64_t qbase = base + a.q_row0 * rs;
+  const int Lq = a.Lq;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, qbase, rs, Lq, D, 2);
   const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
   const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
-  const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), base, rs, L, D,
+  const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), qbase, rs, Lq, D,
                                OUT_F32 ? 4 : 2);
 
   const int lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int row0 = qt * FBM + wave * 32;
-  const bool active = row0 < L;
+  const bool active = row0 < Lq;
   const int n = (L + FBN - 1) / FBN;
   const int nv_last = L - (n - 1) * FBN;
   const float c = a.scale_log2;
@@ -242,8 +245,8 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
-  if (a.lse && h == 0 && row0 + (lane & 31) < L)
-    a.lse[hd * (a.head_elems / D) + base + (row0 + (lane & 31)) * rs] = st.m + __builtin_amdgcn_logf(lsum);
+  if (a.lse && h == 0 && row0 + (lane & 31) < Lq)
+    a.lse[hd * (a.head_elems / D) + qbase + (row0 + (lane & 31)) * rs] = st.m + __builtin_amdgcn_logf(lsum);
   store_out<D, OUT_F32, POLICY>(ro, row0 + (lane & 31), rs, st.o, 1.f / lsum, lane);
 }
 
@@ -297,10 +300,12 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(Grouped
   const int64_t base = problem_base(a, p);
   const int64_t rs = a.row_stride;
   const int L = a.L;
-  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  // queries (and outputs): rows q_row0 .. q_row0 + Lq - 1; keys, values: rows 0 .. L - 1
+  const int64_t qbase = base + a.q_row0 * rs;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, qbase, rs, a.Lq, D, 2);
   const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
   const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
-  const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), base, rs, L, D,
+  const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), qbase, rs, a.Lq, D,
                                OUT_F32 ? 4 : 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
 
@@ -370,7 +375,7 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(Grouped
   }
   const float lsum = halves_sum(l);
   const float inv = 1.f / lsum;
-  if (a.lse && h == 0 && r < L) a.lse[hd * (a.head_elems / D) + base + r * rs] = mx + __builtin_amdgcn_logf(lsum);
+  if (a.lse && h == 0 && r < a.Lq) a.lse[hd * (a.head_elems / D) + qbase + r * rs] = mx + __builtin_amdgcn_logf(lsum);
   if constexpr (OUT_F32) {
     store_out<D, true>(ro, r, rs, o, inv, lane);
   } else {
@@ -566,7 +571,7 @@ bool offsets_fit(const GroupedArgs& a, int pad_rows) {
 
 template <int D, bool F32>
 hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
-  const int qtiles = (a.L + FBM - 1) / FBM;
+  const int qtiles = (a.Lq + FBM - 1) / FBM;
   const int64_t nwg = static_cast<int64_t>(qtiles) * a.problems * a.heads;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((flash_kernel<D, F32>), dim3(static_cast<unsigned>(nwg)), dim3(FNT), 0, s, a, qtiles,
@@ -607,7 +612,8 @@ hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
 
 bool fused_supported(const GroupedArgs& s1, const GroupedArgs& s2) {
   return flash_supported(s1) && s1.o_type == kBF16 && mfma_types_ok(s2) && s2.o_type == kBF16 && s2.D == s1.D &&
-         s2.L >= 2 && s2.L <= 32 && offsets_fit(s2, 32);
+         s2.L >= 2 && s2.L <= 32 && offsets_fit(s2, 32) && s1.q_row0 == 0 && s1.Lq == s1.L && s2.q_row0 == 0 &&
+         s2.Lq == s2.L;
 }
 
 int64_t fused_ctl_ints(int64_t heads, int64_t tiles) { return kCtlReady + heads * tiles; }

@@ -98,6 +98,7 @@ __global__ void __launch_bounds__(256) tiny_kernel(GroupedArgs a, int64_t total)
 #pragma unroll
   for (int i = 0; i < LMAX; ++i) {
     if (i >= L) break;
+    if (i < a.q_row0 || i >= a.q_row0 + a.Lq) continue;
     const int64_t row = head + (base + i * a.row_stride) * D + ch;
     float q[8];
     load8(q, a.q, row, a.qk_type);

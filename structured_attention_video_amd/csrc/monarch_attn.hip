@@ -68,6 +68,8 @@ GroupedArgs stage1_args(const monarch_plan_info& p, const void* q, const void* k
   a.outer = p.b;
   a.row_stride = 1;
   a.L = static_cast<int32_t>(p.b);
+  a.q_row0 = 0;
+  a.Lq = a.L;
   a.D = static_cast<int32_t>(p.head_dim);
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.qk_type = as_elem(p.dtype);
@@ -88,6 +90,8 @@ GroupedArgs stage2_args(const monarch_plan_info& p, const void* q, const void* k
   a.outer = p.tau;
   a.row_stride = p.b;
   a.L = static_cast<int32_t>(p.m_tau);
+  a.q_row0 = 0;
+  a.Lq = a.L;
   a.D = static_cast<int32_t>(p.head_dim);
   a.scale_log2 = p.scale * 1.4426950408889634f;
   a.qk_type = as_elem(p.dtype);
@@ -306,6 +310,47 @@ monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, cons
   const int64_t io = tensor_bytes(p, p.dtype), ny = tensor_bytes(p, ydt);
   if (overlap(o, io, q, io) || overlap(o, io, k, io) || overlap(o, io, y, ny)) return MONARCH_ERR_ALIAS;
   return run_stage2(p, q, k, y, ydt, o, static_cast<hipStream_t>(stream));
+}
+
+monarch_status monarch_attn_chunk_forward(const monarch_plan* plan, int32_t t0, int32_t t1, const void* q,
+                                          const void* k, const void* v, void* y, void* o, void* stream) {
+  if (!plan || !q || !k || !v || !o) return MONARCH_ERR_INVALID_ARG;
+  const monarch_plan_info& p = plan->info;
+  if (t0 < 0 || t1 <= t0 || t1 > p.T) return MONARCH_ERR_INVALID_ARG;
+  const int64_t frame = p.H * p.W;
+  // chunks must consist of whole blocks, and stage 2 must span the whole video
+  if (p.tiles != 1 || frame % p.b != 0) return MONARCH_ERR_UNSUPPORTED;
+  const bool has1 = p.b > 1, has2 = p.m_tau > 1;
+  if (!has2) return MONARCH_ERR_UNSUPPORTED;  // b = N: the one block is the whole video
+  if (has1 && !y) return MONARCH_ERR_INVALID_ARG;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || (y && misaligned(y)))
+    return MONARCH_ERR_UNALIGNED;
+  const int64_t io = tensor_bytes(p, p.dtype), ny = tensor_bytes(p, p.y_dtype);
+  if (overlap(o, io, q, io) || overlap(o, io, k, io) || overlap(o, io, v, io)) return MONARCH_ERR_ALIAS;
+  if (y && has1 && (overlap(y, ny, o, io) || overlap(y, ny, q, io) || overlap(y, ny, k, io) ||
+                    overlap(y, ny, v, io)))
+    return MONARCH_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t bpf = frame / p.b;  // blocks per frame
+  const int64_t r0 = t0 * bpf, r1 = t1 * bpf;  // block rows of the chunk
+  if (has1) {
+    // stage 1 on the chunk's blocks only: the same problems, shifted
+    const int64_t shift = r0 * p.b * p.head_dim;
+    const size_t e = elem_bytes(p.dtype), ey = elem_bytes(p.y_dtype);
+    GroupedArgs a = stage1_args(p, static_cast<const char*>(q) + shift * e, static_cast<const char*>(k) + shift * e,
+                                static_cast<const char*>(v) + shift * e, static_cast<char*>(y) + shift * ey,
+                                p.y_dtype);
+    a.problems = static_cast<int32_t>(r1 - r0);
+    if (launch(choose_kernel(a, p.flags), a, s) != hipSuccess) return MONARCH_ERR_HIP;
+  }
+  // stage 2: every group keeps the rows of blocks 0 .. r1-1 as keys and values
+  // (earlier chunks' Y from the cache), and only the chunk's rows query
+  GroupedArgs a = stage2_args(p, q, k, has1 ? y : v, has1 ? p.y_dtype : p.dtype, o);
+  a.L = static_cast<int32_t>(r1);
+  a.q_row0 = static_cast<int32_t>(r0);
+  a.Lq = static_cast<int32_t>(r1 - r0);
+  return launch(choose_kernel(a, p.flags), a, s) == hipSuccess ? MONARCH_OK : MONARCH_ERR_HIP;
 }
 
 size_t monarch_attn_backward_workspace_size(const monarch_plan* plan) {

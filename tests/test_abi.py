@@ -261,3 +261,24 @@ def test_backward_argument_errors():
     st, h = _plan(heads=2, grid=(4, 6, 10), dtype=1)
     assert L.monarch_attn_backward(h, *ptr[:8], ws, 1 << 30, None) == _lib.ERR_UNSUPPORTED
     L.monarch_attn_destroy(h)
+
+
+# ------------------------------------------------------------------ chunk forward
+def test_chunk_forward_argument_errors():
+    F = 1 << 36
+    ptr = [F + i * (1 << 30) for i in range(5)]  # q, k, v, y, o
+    st, h = _plan(heads=2, grid=(4, 6, 10))
+    call = lambda t0, t1, p=ptr: L.monarch_attn_chunk_forward(h, t0, t1, *p, None)
+    assert call(-1, 2) == _lib.ERR_INVALID_ARG
+    assert call(2, 2) == _lib.ERR_INVALID_ARG
+    assert call(1, 5) == _lib.ERR_INVALID_ARG          # t1 > T
+    assert call(0, 2, [0] + ptr[1:]) == _lib.ERR_INVALID_ARG
+    assert call(0, 2, ptr[:3] + [0, ptr[4]]) == _lib.ERR_INVALID_ARG   # y needed when b > 1
+    assert call(0, 2, [ptr[0] + 2] + ptr[1:]) == _lib.ERR_UNALIGNED
+    assert call(0, 2, ptr[:4] + [ptr[1] + 64]) == _lib.ERR_ALIAS       # o overlaps k
+    L.monarch_attn_destroy(h)
+    for kw in (dict(tile=120), dict(align=2)):  # tiled; dense (one block = the whole video)
+        st, h = _plan(heads=2, grid=(4, 6, 10), **kw)
+        assert st == _lib.OK
+        assert L.monarch_attn_chunk_forward(h, 0, 2, *ptr, None) == _lib.ERR_UNSUPPORTED
+        L.monarch_attn_destroy(h)

@@ -1,0 +1,72 @@
+"""GPU parity of one frame-causal chunk (monarch_attn_chunk_forward) against
+the pinned chunk oracle; the whole video as one chunk equals the forward
+bit for bit; frames from t1 on have no influence (bit for bit)."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from structured_attention_video_amd import MonarchPlan
+from gpu_util import assert_close, say, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BF16, F32 = torch.bfloat16, torch.float32
+
+
+def chunks(plan, q, k, v, bounds):
+    """Run the chunks in order (each reads the Y cache the earlier ones wrote)."""
+    y = torch.zeros(q.shape, dtype=plan.y_dtype, device=DEV) if plan.info["b"] > 1 else None
+    o = torch.full_like(q, float("nan"))
+    for t0, t1 in bounds:
+        plan.chunk_forward(q, k, v, y, o, t0, t1)
+    torch.cuda.synchronize()
+    return o
+
+
+CASES = [
+    # (grid, d, dtype, align, chunk frames)
+    ((6, 4, 37), 128, BF16, "frame", 2),   # b=148 (flash stage 1), groups of up to 6 rows
+    ((9, 5, 20), 128, BF16, "frame", 3),   # b=100 (group stage 1)
+    ((8, 4, 9), 64, BF16, "row", 3),       # row alignment: group rows (t, h), d=64
+    ((40, 2, 5), 128, BF16, "frame", 7),   # m=40 > 32 groups, uneven last chunk
+    ((5, 3, 8), 128, F32, "frame", 2),     # fp32 path
+    ((6, 2, 3), 128, BF16, "token", 2),    # b=1: chunk-causal dense attention
+]
+
+
+@pytest.mark.parametrize("grid,d,dtype,align,cf", CASES,
+                         ids=[f"{g[0]}x{g[1]}x{g[2]}-d{d}-{str(t)[6:]}-{a}-c{c}" for g, d, t, a, c in CASES])
+def test_chunks_match_oracle(grid, d, dtype, align, cf):
+    T, H, W = grid
+    q, k, v = datagen.qkv(2, 3, grid, d, (71, 72, 73), dtype=dtype)
+    plan = MonarchPlan(2, 3, d, grid, align=align, dtype=dtype)
+    b = plan.info["b"]
+    bounds = [(t, min(t + cf, T)) for t in range(0, T, cf)]
+    o = to_np(chunks(plan, *(x.to(DEV) for x in (q, k, v)), bounds))
+    for t0, t1 in bounds:
+        want = oracle.monarch_chunk_forward(q, k, v, b, H * W, t0, t1)
+        assert_close(o[:, :, t0 * H * W:t1 * H * W], want, dtype, f"chunk {t0}-{t1}")
+
+
+def test_whole_video_chunk_equals_forward_and_future_is_ignored():
+    name = "frame_bf16"
+    c = datagen.CONFIGS[name]
+    q, k, v = (x.to(DEV) for x in datagen.config_inputs(name, heads=2))
+    plan = MonarchPlan(1, 2, 128, c["grid"], align="frame")
+    full = plan.forward(q, k, v)
+    one = chunks(plan, q, k, v, [(0, 21)])
+    assert torch.equal(one, full)
+    # the last three frames as a chunk, after the cache of frames 0..17
+    o = chunks(plan, q, k, v, [(0, 18), (18, 21)])
+    hw = 30 * 52
+    want = oracle.monarch_chunk_forward(q.cpu(), k.cpu(), v.cpu(), hw, hw, 18, 21)
+    assert_close(to_np(o)[:, :, 18 * hw:], want, BF16, "frames 18-20 after a cache of 18 frames")
+    # frames after the chunk: replaced, the chunk's output does not change at all
+    q2, k2, v2 = (x.clone() for x in (q, k, v))
+    for x in (q2, k2, v2):
+        x[:, :, 12 * hw:] = torch.randn_like(x[:, :, 12 * hw:]) * 3
+    a = chunks(plan, q, k, v, [(0, 9), (9, 12)])
+    b = chunks(plan, q2, k2, v2, [(0, 9), (9, 12)])
+    assert torch.equal(a[:, :, :12 * hw], b[:, :, :12 * hw])
