@@ -51,20 +51,26 @@ struct TileOffsets {
 };
 
 // ---------------------------------------------------------------- flash
-constexpr int FBM = 128;  // query rows per workgroup
+constexpr int FBM = 128;  // query rows per four-wave workgroup
 constexpr int FBN = 64;   // keys per LDS tile
-constexpr int FNT = 256;  // threads
+constexpr int FNT = 256;  // threads of a four-wave workgroup
 
 // LDS tiles of the flash kernel: 64 rows x D channels, rows unpadded, the
 // 16-byte chunks of row r permuted by c -> c ^ swz(r). Tiles are filled by
 // buffer loads that write LDS directly (64 lanes x 16 bytes = one contiguous
 // kilobyte per instruction; lane i fetches the global chunk that belongs in
 // slot i). The swizzle keeps every 16-lane phase of the 16-byte K reads and
-// of the transposing V reads on distinct banks.
+// every 32-lane phase of the transposing V reads on distinct banks: a
+// transposing read touches rows 4q..4q+3 of one 16-row step, and the low two
+// row bits pick the high chunk bits (D = 128, 16 chunks: a 4x4 bit transpose
+// of r mod 16; D = 64, 8 chunks, two rows per 256-byte bank line: row bit 1
+// picks the top chunk bit). The previous choice, which XORed 2r into the
+// chunk index, left pairs of those rows on one bank group and doubled the
+// transposing reads' LDS cycles (measured with SQ_LDS_BANK_CONFLICT).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) return ((2 * r) & 15) | ((r >> 3) & 1);
-  else return (2 * ((r >> 1) & 3)) | ((r >> 3) & 1);
+  if constexpr (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 template <int D>
@@ -125,6 +131,30 @@ struct FlashOffsets {
 #pragma unroll
     for (int i = 0; i < T::IPW; ++i)
       lds_dma16(src, tile + (16 * wave + T::RPI * i) * T::ROWB, src_off[i] + tile_off);
+  }
+};
+
+// One wave's share of a 64-row tile copy when NW waves split it: rows
+// RW*wave .. +RW, 16 bytes per lane per instruction (the same slot mapping
+// as FlashOffsets::dma, which is the NW = 4 case).
+template <int D, int NW>
+struct TileDma {
+  using T = SwTile<D>;
+  static constexpr int RW = FBN / NW;      // rows per wave
+  static constexpr int IPW = RW / T::RPI;  // copy instructions per wave per tile
+  static_assert(IPW >= 1 && RW % T::RPI == 0, "tile rows must split evenly over the waves");
+  uint32_t src_off[IPW];  // global, relative to the tile's first row
+  __device__ __forceinline__ TileDma(int wave, int lane, int64_t rs) {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = RW * wave + T::RPI * i + lane / T::CPR;
+      const int c = (lane % T::CPR) ^ swz<D>(row);
+      src_off[i] = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void dma(char* tile, __amdgpu_buffer_rsrc_t src, uint32_t tile_off, int wave) const {
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) lds_dma16(src, tile + (RW * wave + T::RPI * i) * T::ROWB, src_off[i] + tile_off);
   }
 };
 

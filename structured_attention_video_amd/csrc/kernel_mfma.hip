@@ -27,12 +27,23 @@ namespace {
 
 using namespace mfma;
 
-// Running max update with lazy rescale of the accumulator.
+// max of three (one v_max3_f32)
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
+// Running max update with lazy rescale of the accumulator. The tile maximum
+// is a max3 tree over the lane's 32 scores (16 instructions).
 template <int D>
 __device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m, float& l, float c) {
-  float mx = fmaxf(s[0][0], s[1][0]);
+  float t[12];
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s[0][i], s[1][i]));
+  for (int i = 0; i < 10; ++i) {
+    const int a = 3 * i, b = 3 * i + 1, e = 3 * i + 2;
+    t[i] = max3(s[a >> 4][a & 15], s[b >> 4][b & 15], s[e >> 4][e & 15]);
+  }
+  t[10] = s[1][14];
+  t[11] = s[1][15];
+  const float mx4 = max3(max3(t[0], t[1], t[2]), max3(t[3], t[4], t[5]), max3(t[6], t[7], t[8]));
+  float mx = fmaxf(mx4, max3(t[9], t[10], t[11]));
   mx = halves_max(mx) * c;
   if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold)) {
     const float mn = fmaxf(m, mx);
@@ -42,6 +53,15 @@ __device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D /
     for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
     m = mn;
   }
+}
+
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// l += a + b over a pair of bf16 weights (one v_dot2c_f32_bf16): the row sum
+// then adds exactly the rounded weights the value product uses.
+__device__ __forceinline__ float sum2(bf16x2 p, float l) {
+  const bf16x2 one = {static_cast<bf16>(1.0f), static_cast<bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, one, l, false);
 }
 
 template <int D>
@@ -65,10 +85,10 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
                                                   const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
                                                   bf16x8 (&pb)[4], float& l, float c, float m) {
   constexpr int KS = D / 16;
-  constexpr int PER = 32 / KS;
+  constexpr int PER = 32 / KS;  // weights per step, even
   sn[0] = f32x16{};
   sn[1] = f32x16{};
-  float p[32];
+  bf16x2 pp[16];
   bf16x8 a0 = k_operand<D>(kl, fo, 0, 0), a1 = k_operand<D>(kl, fo, 0, 1);
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
@@ -80,10 +100,12 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
     sn[0] = mma(a0, qf[ks], sn[0]);
     sn[1] = mma(a1, qf[ks], sn[1]);
 #pragma unroll
-    for (int e = 0; e < PER; ++e) {
+    for (int e = 0; e < PER; e += 2) {
       const int i = ks * PER + e;
-      p[i] = fast_exp2(fmaf(s[i >> 4][i & 15], c, -m));
-      l += p[i];
+      const float p0 = fast_exp2(fmaf(s[i >> 4][i & 15], c, -m));
+      const float p1 = fast_exp2(fmaf(s[(i + 1) >> 4][(i + 1) & 15], c, -m));
+      pp[i >> 1] = bf16x2{static_cast<bf16>(p0), static_cast<bf16>(p1)};
+      l = sum2(pp[i >> 1], l);
     }
     __builtin_amdgcn_sched_barrier(0);
     a0 = n0;
@@ -91,20 +113,25 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
   }
 #pragma unroll
   for (int st = 0; st < 4; ++st)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) pb[st][e] = static_cast<bf16>(p[8 * st + e]);
+    pb[st] = __builtin_shufflevector(__builtin_shufflevector(pp[4 * st], pp[4 * st + 1], 0, 1, 2, 3),
+                                     __builtin_shufflevector(pp[4 * st + 2], pp[4 * st + 3], 0, 1, 2, 3), 0, 1, 2,
+                                     3, 4, 5, 6, 7);
 }
 
 // exp2(s*c - m) as bf16 B operands for the four 16-key PV steps (last tile)
 __device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float c, float m) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
+    bf16x2 pp[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = fast_exp2(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m));
-      l += p;
-      pb[st][e] = static_cast<bf16>(p);
+    for (int e = 0; e < 8; e += 2) {
+      const float p0 = fast_exp2(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m));
+      const float p1 = fast_exp2(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c, -m));
+      pp[e >> 1] = bf16x2{static_cast<bf16>(p0), static_cast<bf16>(p1)};
+      l = sum2(pp[e >> 1], l);
     }
+    pb[st] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                     __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
   }
 }
 
@@ -139,24 +166,27 @@ __device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vl, const 
 #define MONARCH_PRIO 2
 #endif
 
-// Mutable per-wave state of the flash loop.
+// Mutable per-wave state of the flash loop (the raw scores of the current
+// tile alternate between two register sets, sa and sb, so that no copy is
+// needed between iterations).
 template <int D>
 struct FlashState {
-  f32x16 s[2];       // scores of the current tile (raw)
   f32x16 o[D / 32];  // O^T accumulators
   float m, l;        // running max (scaled) and partial sum
-
 };
 
-// Query tile qt (128 rows) of problem p of head hd. The LDS slots are four
-// separate __shared__ arrays of the calling kernel (not fields of one): the
-// compiler then proves that reads of one slot never alias the asynchronous
-// copy into another and waits for the copies only at the barriers. Every
-// copy it issues has completed when it returns; waves whose rows lie past
-// the end of the problem return early (after the last barrier).
-template <int D, bool OUT_F32, int POLICY = 0>
-__device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, int qt, char* k0, char* k1,
-                                           char* v0, char* v1, int tid) {
+// Query tile qt (rows qt*qrows .. +qrows, qrows a multiple of 32 and at most
+// 32*NW) of problem p of head hd, computed by NW waves: wave w owns rows
+// 32w .. 32w+31 of the tile and all NW waves share the tile copies. The LDS
+// slots are four separate __shared__ arrays of the calling kernel (not
+// fields of one): the compiler then proves that reads of one slot never
+// alias the asynchronous copy into another and waits for the copies only at
+// the barriers. Every copy it issues has completed when it returns; waves
+// whose rows lie outside the tile or past the end of the problem only copy,
+// and return early (after the last barrier).
+template <int D, bool OUT_F32, int POLICY = 0, int NW = 4>
+__device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, int qt, int qrows, char* k0,
+                                           char* k1, char* v0, char* v1, int tid) {
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
   const int64_t base = problem_base(a, p);
   const int64_t rs = a.row_stride;
@@ -170,19 +200,21 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   const auto ro = problem_rsrc(static_cast<const char*>(a.o) + hoff * (OUT_F32 ? 4 : 2), qbase, rs, Lq, D,
                                OUT_F32 ? 4 : 2);
 
-  const int lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int row0 = qt * FBM + wave * 32;
-  const bool active = row0 < Lq;
+  const int lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses stay scalar
+  const int row0 = qt * qrows + wave * 32;
+  const bool active = wave * 32 < qrows && row0 < Lq;
   const int n = (L + FBN - 1) / FBN;
   const int nv_last = L - (n - 1) * FBN;
   const float c = a.scale_log2;
-  const FlashOffsets<D> fo(wave, lane, rs);
+  const FlashOffsets<D> fo(wave, lane, rs);  // LDS read offsets
+  const TileDma<D, NW> td(wave, lane, rs);
   const uint32_t tile_bytes = static_cast<uint32_t>(FBN * rs * D * 2);
 
   // prologue: K tiles 0 and 1, V tile 0
-  fo.dma(k0, rk, 0, wave);
-  fo.dma(v0, rv, 0, wave);
-  if (n > 1) fo.dma(k1, rk, tile_bytes, wave);
+  td.dma(k0, rk, 0, wave);
+  td.dma(v0, rv, 0, wave);
+  if (n > 1) td.dma(k1, rk, tile_bytes, wave);
   bf16x8 qf[D / 16];
   load_qfrag<D>(qf, rq, row0, rs, lane);
   FlashState<D> st;
@@ -193,26 +225,28 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   wait_dma();
   __syncthreads();
 
-  if (active) scores64<D>(st.s, k0, fo, qf);
+  f32x16 sa[2], sb[2];
+  if (active) scores64<D>(sa, k0, fo, qf);
   // iteration 0 refills K slot 0 (tile 0): every wave must be done with it
   __syncthreads();
 
   // Iteration j: copy K_{j+2} into kdma and V_{j+1} into vdma (global ->
-  // LDS, asynchronous), then the scores of tile j+1 from kread while the
-  // softmax of tile j runs, then its value product from vread. The four LDS
-  // slots are distinct fields so the compiler can see that the reads never
-  // touch the tiles being copied and does not wait for the copies first.
-  auto step = [&](int j, char* kdma, char* vdma, const char* kread, const char* vread) {
-    if (j + 2 < n) fo.dma(kdma, rk, (j + 2) * tile_bytes, wave);
-    fo.dma(vdma, rv, (j + 1) * tile_bytes, wave);
+  // LDS, asynchronous), then the scores of tile j+1 (into sn) from kread
+  // while the softmax of tile j (scores s) runs, then its value product from
+  // vread. The four LDS slots are distinct fields so the compiler can see
+  // that the reads never touch the tiles being copied and does not wait for
+  // the copies first.
+  auto step = [&](int j, char* kdma, char* vdma, const char* kread, const char* vread, const f32x16 (&s)[2],
+                  f32x16 (&sn)[2]) {
+    if (j + 2 < n) td.dma(kdma, rk, (j + 2) * tile_bytes, wave);
+    td.dma(vdma, rv, (j + 1) * tile_bytes, wave);
     if (active) {
-      update_max<D>(st.s, st.o, st.m, st.l, c);
-      f32x16 sn[2];
+      update_max<D>(s, st.o, st.m, st.l, c);
       bf16x8 pb[4];
 #if MONARCH_PRIO == 2
       __builtin_amdgcn_s_setprio(1);
 #endif
-      scores_with_probs<D>(sn, kread, fo, qf, st.s, pb, st.l, c, st.m);
+      scores_with_probs<D>(sn, kread, fo, qf, s, pb, st.l, c, st.m);
 #if MONARCH_PRIO == 1
       __builtin_amdgcn_s_setprio(1);
 #endif
@@ -220,28 +254,29 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
 #if MONARCH_PRIO
       __builtin_amdgcn_s_setprio(0);
 #endif
-      st.s[0] = sn[0];
-      st.s[1] = sn[1];
     }
     wait_dma();
     __syncthreads();
   };
 
   // steady state, two iterations per trip so every slot is a fixed array:
-  // even j copies into (k0, v1) and reads (k1, v0); odd j the reverse
+  // even j copies into (k0, v1) and reads (k1, v0), scores sa -> sb; odd j
+  // the reverse
   int j = 0;
   for (; j + 2 < n; j += 2) {
-    step(j, k0, v1, k1, v0);
-    step(j + 1, k1, v0, k0, v1);
+    step(j, k0, v1, k1, v0, sa, sb);
+    step(j + 1, k1, v0, k0, v1, sb, sa);
   }
-  if (j + 1 < n) step(j, k0, v1, k1, v0);
+  const bool odd = j + 1 < n;
+  if (odd) step(j, k0, v1, k1, v0, sa, sb);
 
   if (!active) return;
   // last tile: mask keys past the end, skip the empty half of the PV product
-  if (nv_last < FBN) mask_tail(st.s, nv_last, h);
-  update_max<D>(st.s, st.o, st.m, st.l, c);
+  f32x16 sl[2] = {odd ? sb[0] : sa[0], odd ? sb[1] : sa[1]};
+  if (nv_last < FBN) mask_tail(sl, nv_last, h);
+  update_max<D>(sl, st.o, st.m, st.l, c);
   bf16x8 pb[4];
-  probs(st.s, pb, st.l, c, st.m);
+  probs(sl, pb, st.l, c, st.m);
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
@@ -250,8 +285,14 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   store_out<D, OUT_F32, POLICY>(ro, row0 + (lane & 31), rs, st.o, 1.f / lsum, lane);
 }
 
+// Waves per workgroup of the flash kernel: four (two workgroups per CU).
+// Eight-wave workgroups halve the tile copies per CU but measured slower:
+// the two waves sharing a SIMD then belong to one workgroup and meet at
+// every barrier, so their MFMA and softmax phases stop overlapping.
+constexpr int kFlashWaves = 4;
+
 template <int D, bool OUT_F32>
-__global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles, int nwg) {
+__global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs a, int qtiles, int qrows, int nwg) {
   using T = SwTile<D>;
   __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
   __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
@@ -260,7 +301,8 @@ __global__ void __launch_bounds__(FNT, 2) flash_kernel(GroupedArgs a, int qtiles
   const int id = xcd_order(blockIdx.x, nwg);
   const int qt = id % qtiles;
   const int rest = id / qtiles;
-  flash_tile<D, OUT_F32>(a, rest / a.problems, rest % a.problems, qt, k0, k1, v0, v1, threadIdx.x);
+  flash_tile<D, OUT_F32, 0, kFlashWaves>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1, v0, v1,
+                                         threadIdx.x);
 }
 
 // ---------------------------------------------------------------- group
@@ -521,7 +563,7 @@ __global__ void __launch_bounds__(FNT, 2) fused_kernel(FusedArgs f, int qtiles, 
       const int id = b1 + t;
       const int qt = id % qtiles, rest = id / qtiles;
       const int p = rest % f.s1.problems, hd = rest / f.s1.problems;
-      flash_tile<D, false, kPolicyDevice>(f.s1, hd, p, qt, k0, k1, v0, v1, otid);
+      flash_tile<D, false, kPolicyDevice>(f.s1, hd, p, qt, FBM, k0, k1, v0, v1, otid);
       wait_dma();  // this wave's written-through Y stores have completed
       __syncthreads();
       if (tid == 0)
@@ -571,11 +613,16 @@ bool offsets_fit(const GroupedArgs& a, int pad_rows) {
 
 template <int D, bool F32>
 hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
-  const int qtiles = (a.Lq + FBM - 1) / FBM;
+  // query rows in units of one wave's 32, spread evenly over the fewest
+  // tiles of at most kFlashWaves units (a 1560-row block: 7 tiles of 224)
+  const int units = (a.Lq + 31) / 32;
+  if (units <= 0) return hipErrorInvalidConfiguration;
+  const int qtiles = (units + kFlashWaves - 1) / kFlashWaves;
+  const int qrows = 32 * ((units + qtiles - 1) / qtiles);
   const int64_t nwg = static_cast<int64_t>(qtiles) * a.problems * a.heads;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((flash_kernel<D, F32>), dim3(static_cast<unsigned>(nwg)), dim3(FNT), 0, s, a, qtiles,
-                     static_cast<int>(nwg));
+  hipLaunchKernelGGL((flash_kernel<D, F32>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0, s, a,
+                     qtiles, qrows, static_cast<int>(nwg));
   return hipGetLastError();
 }
 
