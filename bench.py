@@ -51,6 +51,9 @@ def parse():
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the forward only: skip the other forward variant, the backward, the chunk and "
+                         "the dense comparison (profiling runs: every launch of a kernel is then the same workload)")
     ap.add_argument("--fused", choices=["auto", "on", "off"], default="off",
                     help="one fused launch for both stages: where it applies (auto), required (on), "
                          "never (off, the default: the two-launch path measures faster)")
@@ -196,14 +199,26 @@ def main():
     per_call = timed(call, args.steps)
     pct = lambda xs, f: xs[min(len(xs) - 1, int(f * len(xs)))]
 
-    # per-stage times of the two-launch path (context, and the roofline when not fused)
+    # per-stage times of the two-launch path (context, and the roofline when not
+    # fused): the two launches alternate as in a forward call, with HIP events
+    # between them, so each launch runs in the conditions of the timed calls
+    # (back-to-back launches of one stage alone run hotter and slower)
     stage_ms = {}
     if has1 and has2:
         for _ in range(2):
             split.stage1(q, k, v, y)
             split.stage2(q, k, y, o)
-        t1 = timed(lambda: split.stage1(q, k, v, y), args.steps)
-        t2 = timed(lambda: split.stage2(q, k, y, o), args.steps)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e in ev:
+            e[0].record()
+            split.stage1(q, k, v, y)
+            e[1].record()
+            split.stage2(q, k, y, o)
+            e[2].record()
+        torch.cuda.synchronize()
+        t1 = [e[0].elapsed_time(e[1]) for e in ev]
+        t2 = [e[1].elapsed_time(e[2]) for e in ev]
         stage_ms = {"stage1": sum(t1) / len(t1), "stage2": sum(t2) / len(t2)}
         call()  # leave o = the measured path's output
     else:
@@ -280,7 +295,7 @@ def main():
 
     # the other forward variant (fused one-launch vs two launches), for context
     alt = mk(not plan.fused)
-    if alt.fused != plan.fused:
+    if alt.fused != plan.fused and not args.forward_only:
         alt_ws = alt.new_workspace(dev)
         oa = torch.empty_like(q)
         for _ in range(2):
@@ -296,7 +311,7 @@ def main():
     # time per call and the rate at 2.5x the forward FLOPs (five products of the
     # forward's size: the usual accounting for attention backward; the library
     # additionally recomputes the forward)
-    if split.backward_workspace_bytes:
+    if split.backward_workspace_bytes and not args.forward_only:
         bws = torch.empty(split.backward_workspace_bytes, dtype=torch.uint8, device=dev)
         go = torch.randn(q.shape, generator=torch.Generator().manual_seed(77)).to(dt).to(dev)
         gq, gk, gv = (torch.empty_like(q) for _ in range(3))
@@ -312,7 +327,8 @@ def main():
     # one frame-causal chunk (the last three frames against the cache of all earlier
     # frames: autoregressive generation, three frames per chunk) at the same shape
     T = c["grid"][0]
-    if info["tiles"] == 1 and info["m_tau"] > 1 and T >= 4 and (c["grid"][1] * c["grid"][2]) % info["b"] == 0:
+    if (info["tiles"] == 1 and info["m_tau"] > 1 and T >= 4 and (c["grid"][1] * c["grid"][2]) % info["b"] == 0
+            and not args.forward_only):
         yc = torch.zeros(q.shape, dtype=split.y_dtype, device=dev) if info["b"] > 1 else None
         oc = torch.empty_like(q)
         split.chunk_forward(q, k, v, yc, oc, 0, T - 3)
@@ -322,7 +338,7 @@ def main():
         out["chunk"] = {"frames": [T - 3, T], "cached_frames": T - 3, "ms_per_call_p50": round(pct(tc, 0.5), 4)}
         del yc, oc
 
-    if not args.no_dense:
+    if not args.no_dense and not args.forward_only:
         dplan = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align="dense", dtype=dt)
         od = torch.empty_like(q)
         dplan.forward(q, k, v, out=od)
