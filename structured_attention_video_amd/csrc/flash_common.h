@@ -73,6 +73,12 @@ __device__ __forceinline__ int swz(int r) {
   else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
+// byte offset of 16-byte chunk c of row r in a swizzled tile of unpadded rows
+template <int D>
+__device__ __forceinline__ int swoff(int r, int c) {
+  return r * D * 2 + 16 * (c ^ swz<D>(r));
+}
+
 template <int D>
 struct SwTile {
   static constexpr int ROWB = D * 2;          // bytes per row

@@ -61,9 +61,18 @@ struct BwdArgs {
   const float* dq_in;
   const float* dk_in;
   ElemType dq_type, dk_type, dv_type;
+  float* dv_delta;  // one-pass small-problem backward only: per row, sum over channels of
+                    // the stored (rounded) dV times the stage's values v
 };
 bool bwd_supported(const GroupedArgs& g);
 hipError_t launch_bwd(const BwdArgs& b, hipStream_t stream);
+// One-pass backward of a stage whose problems have at most 32 rows (the frame
+// stage-2 groups): one wave per problem recomputes the forward (its own lse and
+// fp32 output, so lse and delta are not inputs), forms dQ, dK (fp32) and dV
+// (bf16), and writes dv_delta for the next stage's backward. Needs go, dq, dk,
+// dv, dv_delta; lse, delta, dq_in and dk_in are not used.
+bool bwd_small_supported(const GroupedArgs& g);
+hipError_t launch_bwd_small(const BwdArgs& b, hipStream_t stream);
 // out[r] = sum_c a[r][c] * b[r][c] over rows x D (bf16 or fp32 elements)
 hipError_t launch_rowdot(const void* a, ElemType ta, const void* b, ElemType tb, float* out, int64_t rows, int D,
                          hipStream_t stream);

@@ -290,6 +290,187 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   else store_rows<D>(rdv, vf32, ra, false, r, rs, acc, 1.f, lane);
 }
 
+// ---------------------------------------------------------------- small problems, one pass
+// One wave per problem of at most 32 rows (the frame layout's stage-2 groups,
+// m = 21), everything in one launch. Q, K, V (the stage's values) and G rows
+// are copied whole into four swizzled 32-row LDS tiles; every product is one
+// 32x32 tile. The wave
+//   (a) recomputes the forward with lane = query: S^T = K Q^T, its row max
+//       and sum (so lse) and P^T; dP^T = V G^T; delta = rowsum(G * O) as the
+//       sum over keys of P dP; dS^T = P^T (dP^T - delta); dQ^T = K^T dS^T;
+//   (b) with lane = key, taking lse and delta of each query from LDS:
+//       S = Q K^T, dP = G V^T, P, dS, dV^T = G^T P and dK^T = Q^T dS, and
+//       the next stage's delta of each key row, rowsum(dV * V) with dV
+//       rounded as stored.
+// Recomputing S and dP in the second layout costs 16 MFMAs per problem,
+// nothing against its memory traffic; the launch replaces the stage's
+// forward recompute, both row-dot launches and the three tiled backward
+// launches.
+// Rows past the end read as zero (keys masked in (a); queries have zero G,
+// so zero dS; results of rows past the end are dropped at the store).
+// Sum over this lane's channels of x^T (register i of tile mt: channel
+// 32 mt + 8 (i / 4) + 4 h + i % 4), scaled by mul and optionally rounded to
+// bf16, times the same channels of row r of a bf16 tile.
+template <int D>
+__device__ __forceinline__ float row_dot_acc(const f32x16 (&x)[D / 32], float mul, bool round_bf16,
+                                             const char* tile, int r, int h) {
+  constexpr int ROWB = D * 2;
+  float acc = 0.f;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(tile + r * ROWB + 16 * ((4 * mt + g) ^ swz<D>(r)) + 8 * h);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t bits = (e & 1) ? (w[e >> 1] & 0xffff0000u) : (w[e >> 1] << 16);
+        float xv = x[mt][4 * g + e] * mul;
+        if (round_bf16) xv = static_cast<float>(static_cast<bf16>(xv));
+        acc = fmaf(xv, __uint_as_float(bits), acc);
+      }
+    }
+  return acc;
+}
+
+template <int D>
+__global__ void __launch_bounds__(64) bwd_small_kernel(BwdArgs b) {
+  constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * ROWB;
+  __shared__ __attribute__((aligned(1024))) char qt[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt[TILE];
+  __shared__ __attribute__((aligned(1024))) char vt[TILE];
+  __shared__ __attribute__((aligned(1024))) char gt[TILE];
+  __shared__ float st_lse[32], st_del[32];
+  const GroupedArgs& a = b.g;
+  const int p = blockIdx.x % a.problems, hd = blockIdx.x / a.problems;
+  const int64_t ntok = a.head_elems / D;
+  const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
+  const int64_t base = problem_base(a, p);
+  const int64_t rs = a.row_stride;
+  const int L = a.L;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
+  const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
+  const auto rg = problem_rsrc(static_cast<const bf16*>(b.go) + hoff, base, rs, L, D, 2);
+  const auto rdq = problem_rsrc(static_cast<const char*>(b.dq) + hoff * 4, base, rs, L, D, 4);
+  const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * 4, base, rs, L, D, 4);
+  const auto rdv = problem_rsrc(static_cast<const char*>(b.dv) + hoff * 2, base, rs, L, D, 2);
+  const int lane = threadIdx.x, h = lane >> 5, r = lane & 31;
+  const float c = a.scale_log2;
+
+#pragma unroll
+  for (int i = 0; i < IPW; ++i) {
+    const int row = RPI * i + lane / CPR;
+    const int ch = (lane % CPR) ^ swz<D>(row);
+    const uint32_t goff = static_cast<uint32_t>((row * rs * D + ch * 8) * 2);
+    const int dst = RPI * i * ROWB;
+    lds_dma16(rq, qt + dst, goff);
+    lds_dma16(rk, kt + dst, goff);
+    lds_dma16(rv, vt + dst, goff);
+    lds_dma16(rg, gt + dst, goff);
+  }
+  wait_dma();
+  __syncthreads();
+  const FlashOffsets<D> fo(0, lane, rs);  // LDS read offsets of a tile's first 32 rows
+
+  // (a) lane = query r
+  {
+    bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = ld_bf16x8(qt + swoff<D>(r, 2 * ks + h));
+      gf[ks] = ld_bf16x8(gt + swoff<D>(r, 2 * ks + h));
+    }
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mma(k_operand<D>(kt, fo, ks, 0), qf[ks], s);
+      dp = mma(k_operand<D>(vt, fo, ks, 0), gf[ks], dp);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (acc_key(i, h) >= L) s[i] = -INFINITY;
+    float mx = s[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
+    mx = halves_max(mx) * c;
+    float l = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      s[i] = fast_exp2(fmaf(s[i], c, -mx));
+      l += s[i];
+    }
+    l = halves_sum(l);
+    const float inv = 1.f / l;
+    // delta = rowsum(G * O) = sum over keys of P dP, taken from the fp32 P and
+    // dP in registers: dS = P (dP - delta) then sums to zero over the keys up
+    // to fp32 rounding (G * O with O built from bf16 weights misses that by a
+    // bf16 rounding of P, which the subtraction amplifies)
+    float pd = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) pd = fmaf(s[i], dp[i], pd);
+    const float del = halves_sum(pd) * inv;
+    if (h == 0) {
+      st_lse[r] = mx + __builtin_amdgcn_logf(l);
+      st_del[r] = del;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dp[i] = s[i] * inv * (dp[i] - del);
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 pb = p_operand(dp, st);
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mma(v_operand<D>(kt, fo, mt, st), pb, dq[mt]);
+    }
+    store_rows<D>(rdq, true, rdq, false, r, rs, dq, c * 0.6931471805599453f, lane);
+  }
+  __syncthreads();
+
+  // (b) lane = key r
+  {
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = ld_bf16x8(kt + swoff<D>(r, 2 * ks + h));
+      vf[ks] = ld_bf16x8(vt + swoff<D>(r, 2 * ks + h));
+    }
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mma(k_operand<D>(qt, fo, ks, 0), kf[ks], s);
+      dp = mma(k_operand<D>(gt, fo, ks, 0), vf[ks], dp);
+    }
+    float lse[16], del[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      lse[i] = st_lse[acc_key(i, h)];
+      del[i] = st_del[acc_key(i, h)];
+    }
+    probs_grads(s, dp, lse, del, c);
+    f32x16 dv[D / 32], dk[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      dv[mt] = f32x16{};
+      dk[mt] = f32x16{};
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 pp = p_operand(s, st), ps = p_operand(dp, st);
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        dv[mt] = mma(v_operand<D>(gt, fo, mt, st), pp, dv[mt]);
+        dk[mt] = mma(v_operand<D>(qt, fo, mt, st), ps, dk[mt]);
+      }
+    }
+    store_rows<D>(rdk, true, rdk, false, r, rs, dk, c * 0.6931471805599453f, lane);
+    store_rows<D>(rdv, false, rdv, false, r, rs, dv, 1.f, lane);
+    const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, r, h));
+    if (h == 0 && r < L) b.dv_delta[hd * ntok + base + r * rs] = d1;
+  }
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) rowdot_kernel(const void* a, int ta, const void* bp, int tb, float* out,
                                                      int64_t rows) {
@@ -337,6 +518,23 @@ hipError_t launch_bwd(const BwdArgs& b, hipStream_t s) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, 0>), dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
     hipLaunchKernelGGL((bwd_dkdv_kernel<64, 1>), dim3(grid), dim3(FNT), 0, s, b, tiles, static_cast<int>(nwg));
   }
+  return hipGetLastError();
+}
+
+bool bwd_small_supported(const GroupedArgs& g) {
+  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L >= 1 && g.L <= 32 &&
+         g.q_row0 == 0 && g.Lq == g.L && (static_cast<int64_t>(32) + 32) * g.row_stride * g.D * 4 < (int64_t{1} << 31);
+}
+
+hipError_t launch_bwd_small(const BwdArgs& b, hipStream_t s) {
+  const GroupedArgs& g = b.g;
+  if (!bwd_small_supported(g) || !b.go || !b.dq || !b.dk || !b.dv || !b.dv_delta) return hipErrorInvalidValue;
+  const int64_t nwg = static_cast<int64_t>(g.problems) * g.heads;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  if (g.D == 128)
+    hipLaunchKernelGGL(bwd_small_kernel<128>, dim3(static_cast<unsigned>(nwg)), dim3(64), 0, s, b);
+  else
+    hipLaunchKernelGGL(bwd_small_kernel<64>, dim3(static_cast<unsigned>(nwg)), dim3(64), 0, s, b);
   return hipGetLastError();
 }
 

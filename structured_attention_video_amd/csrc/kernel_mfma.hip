@@ -323,12 +323,6 @@ struct GroupCfg {
   static constexpr int IPW = 32 / RPI;     // DMA instructions per wave per tile
 };
 
-// byte offset of 16-byte chunk c of row r in a swizzled tile
-template <int D>
-__device__ __forceinline__ int swoff(int r, int c) {
-  return r * D * 2 + 16 * (c ^ swz<D>(r));
-}
-
 template <int D, int QT, bool OUT_F32>
 __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(GroupedArgs a) {
   using G = GroupCfg<D, QT>;

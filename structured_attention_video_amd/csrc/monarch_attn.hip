@@ -399,6 +399,9 @@ monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, co
   const int D = static_cast<int>(p.head_dim);
   const bool has1 = p.b > 1, has2 = p.m_tau > 1;
   auto ok = [](hipError_t e) { return e == hipSuccess; };
+  // stage-2 problems of at most 32 rows (frame layout): one launch does the
+  // stage-2 forward recompute, its backward and stage 1's delta
+  const bool small2 = has1 && has2 && bwd_small_supported(stage2_args(p, q, k, y, MONARCH_BF16, nullptr));
 
   // forward again, keeping Y and the per-row statistics
   GroupedArgs f1{}, f2{};
@@ -407,7 +410,17 @@ monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, co
     f1.lse = lse1;
     if (!ok(launch(choose_kernel(f1, p.flags), f1, s))) return MONARCH_ERR_HIP;
   }
-  if (has2) {
+  if (small2) {
+    BwdArgs b2{};
+    b2.g = stage2_args(p, q, k, y, MONARCH_BF16, nullptr);
+    b2.go = grad_o;
+    b2.dq = dq2; b2.dq_type = kF32;
+    b2.dk = dk2; b2.dk_type = kF32;
+    b2.dv = dy; b2.dv_type = kBF16;
+    b2.dv_delta = del1;
+    if (!ok(launch_bwd_small(b2, s))) return MONARCH_ERR_HIP;
+  }
+  if (has2 && !small2) {
     // values: Y (or V when stage 1 is the identity). The recomputed output is
     // kept in fp32 (in the dQ2 section, free until the stage-2 backward): delta
     // = rowsum(G * O) then uses O before its bf16 rounding, which matters
@@ -417,7 +430,7 @@ monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, co
     f2.lse = lse2;
     if (!ok(launch(choose_kernel(f2, p.flags), f2, s))) return MONARCH_ERR_HIP;
   }
-  if (has2) {
+  if (has2 && !small2) {
     BwdArgs b2{};
     b2.g = f2;
     b2.go = grad_o;
@@ -441,7 +454,7 @@ monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, co
     b1.go = has2 ? dy : grad_o;
     b1.lse = lse1;
     b1.delta = del1;
-    if (!ok(launch_rowdot(b1.go, kBF16, has2 ? y : o, kBF16, del1, rows, D, s))) return MONARCH_ERR_HIP;
+    if (!small2 && !ok(launch_rowdot(b1.go, kBF16, has2 ? y : o, kBF16, del1, rows, D, s))) return MONARCH_ERR_HIP;
     b1.dq = grad_q; b1.dq_type = kBF16;
     b1.dk = grad_k; b1.dk_type = kBF16;
     b1.dv = grad_v; b1.dv_type = kBF16;

@@ -57,6 +57,7 @@ SMALL = [
     ((9, 4, 25), 128, BF16, "frame", 300, 0),   # tiled: m_tau=3, 3 tiles
     ((10, 15, 8), 128, BF16, "row", 0, 0),      # b=8, m=150 (> 128)
     ((2, 9, 33), 128, BF16, "frame", 0, 0),     # m=2, b=297
+    ((2, 10, 27), 128, BF16, "frame", 0, 0),    # b=270: three query tiles of 96 rows, one idle wave each
     ((3, 5, 20), 128, BF16, "dense", 0, 0),     # b=N=300
     ((3, 5, 20), 128, BF16, "token", 0, 0),     # b=1, m=300
     ((4, 6, 10), 128, BF16, "custom", 0, 20),   # unaligned split (ablation)
