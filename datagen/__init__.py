@@ -21,6 +21,9 @@ gist.science explainer, "Problem Statement"):
   query/key logit is a sum of one term per axis (the separable positional
   component the pages describe as exactly preserved by aligned blocks).
   V is iid N(0,1).
+* ``noisy_separable_qkv``: the separable Q and K plus noise * N(0,1) per
+  element (a separate seeded draw); noise sets how far the logits are from
+  separable (0 = exactly separable).
 
 The normal draws are fp32 from a seeded ``torch.Generator`` on the CPU; the
 result is cast to the requested dtype (round-to-nearest-even for bf16). The
@@ -40,6 +43,7 @@ __all__ = [
     "qkv",
     "separable_qkv",
     "iid_qkv",
+    "noisy_separable_qkv",
     "CONFIGS",
     "config_inputs",
 ]
@@ -136,6 +140,16 @@ CONFIGS = {
     "long_bf16": dict(batch=1, heads=12, d=128, grid=(81, 30, 52), align="frame", tile_tokens=0,
                       dtype="bf16", seeds=(2000, 2001, 2002), pe_scale=0.5),
 }
+
+
+def noisy_separable_qkv(batch: int, heads: int, grid: Tuple[int, int, int], d: int,
+                        seed: int, noise: float, dtype: torch.dtype = torch.bfloat16):
+    """separable_qkv (drawn in fp32) plus noise * N(0,1) on Q and K (seed + 1, + 2)."""
+    q, k, v = separable_qkv(batch, heads, grid, d, seed, dtype=torch.float32)
+    if noise:
+        q = q + noise * _randn(q.shape, seed + 1)
+        k = k + noise * _randn(k.shape, seed + 2)
+    return tuple(x.to(dtype).contiguous() for x in (q, k, v))
 
 
 def torch_dtype(name: str) -> torch.dtype:
