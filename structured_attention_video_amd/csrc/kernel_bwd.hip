@@ -169,8 +169,33 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dq_kernel(BwdArgs b, int qtiles, i
   store_rows<D>(ro, f32, ra, b.dq_in != nullptr, r, rs, dq, c * 0.6931471805599453f, lane);
 }
 
+// A per-query bias as one more 16-channel K-step of a product with lane =
+// key: the A operand (rows = queries) carries x of this lane's query row in
+// channels 0 and 1 as two bf16 parts (x = hi + lo to ~2^-18 relative), the
+// B operand (bias_ones) ones in channels 0 and 1, so the accumulator gains x
+// for every key. Lanes of the upper half hold channels 8..15: zeros.
+__device__ __forceinline__ bf16x8 bias_operand(float x, int h) {
+  const bf16 hi = static_cast<bf16>(x);
+  const bf16 lo = static_cast<bf16>(x - static_cast<float>(hi));
+  bf16x8 r = {};
+  r[0] = h == 0 ? hi : static_cast<bf16>(0.f);
+  r[1] = h == 0 ? lo : static_cast<bf16>(0.f);
+  return r;
+}
+__device__ __forceinline__ bf16x8 bias_ones(int h) {
+  bf16x8 r = {};
+  r[0] = static_cast<bf16>(h == 0 ? 1.f : 0.f);
+  r[1] = r[0];
+  return r;
+}
+
 // MODE 0: dV only (S -> P; dV^T += G^T P). MODE 1: dK only (S, dP -> dS;
-// dK^T += Q^T dS). One kernel holding both accumulators, K and V would need
+// dK^T += Q^T dS). In MODE 1 the per-query lse and delta enter the products
+// as a bias K-step (c S - lse and dP - delta come out of the accumulators),
+// so a lane needs only its own query's two values, not one per accumulator
+// register: without it the kernel spilled 25 VGPRs (measured 693 -> 628 us at
+// the frame shape). MODE 0 has registers to spare and reads lse per register
+// (the extra MFMA at the end of its short chain measured slower there). One kernel holding both accumulators, K and V would need
 // more registers than two waves per SIMD have; recomputing S in both costs
 // a quarter more matrix work instead.
 template <int D, int MODE>
@@ -212,6 +237,7 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   // per-row statistics of query tile j (rows past the end: 0), loaded into
   // registers early and stored to LDS slot s just before the barrier
   float nl = 0.f, nd = 0.f;
+  const float inv_c = 1.f / c;
   auto stats_load = [&](int j) {
     if (tid < FBN) {
       const int q = j * FBN + tid;
@@ -232,6 +258,7 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   bf16x8 kf[D / 16], vf[D / 16];
   load_qfrag<D>(kf, rk, key0, rs, lane);
   if (MODE == 1) load_qfrag<D>(vf, rv, key0, rs, lane);
+  const bf16x8 ones = bias_ones(h);  // MODE 1 only
   f32x16 acc[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) acc[mt] = f32x16{};
@@ -254,17 +281,30 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
         s = mma(k_operand<D>(qc, fo, ks, sub), kf[ks], s);
         if (MODE == 1) dp = mma(k_operand<D>(gc, fo, ks, sub), vf[ks], dp);
       }
-      float lse[16], del[16];
+      if (MODE == 1) {
+        // s -= lse / c and dp -= delta (the bias K-step, lane = this query row)
+        const int qrow = 32 * sub + (lane & 31);
+        s = mma(bias_operand(-st_lse[sc][qrow] * inv_c, h), ones, s);
+        dp = mma(bias_operand(-st_del[sc][qrow], h), ones, dp);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int q = 32 * sub + 8 * g + 4 * h;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          lse[4 * g + e] = st_lse[sc][q + e];
-          del[4 * g + e] = MODE == 1 ? st_del[sc][q + e] : 0.f;
+        for (int i = 0; i < 16; ++i) {
+          s[i] = fast_exp2(s[i] * c);  // P
+          dp[i] *= s[i];               // dS = P (dP - delta)
         }
+      } else {
+        // P = exp2(c s - lse) with lse of each register's query
+        float lse[16], del[16];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int q = 32 * sub + 8 * g + 4 * h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lse[4 * g + e] = st_lse[sc][q + e];
+            del[4 * g + e] = 0.f;
+          }
+        }
+        probs_grads(s, dp, lse, del, c);
       }
-      probs_grads(s, dp, lse, del, c);
       // dV^T += G^T P (MODE 0) or dK^T += Q^T dS (MODE 1), two 16-query steps
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
