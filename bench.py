@@ -320,8 +320,15 @@ def main():
             split.backward(q, k, v, ob, go, workspace=bws, grads=(gq, gk, gv))
         tb = timed(lambda: split.backward(q, k, v, ob, go, workspace=bws, grads=(gq, gk, gv)),
                    max(3, args.steps // 5))
+        # from a training forward's saved state (no forward recompute)
+        split.forward_train(q, k, v, out=ob, workspace=bws)
+        ts = timed(lambda: split.backward(q, k, v, ob, go, workspace=bws, grads=(gq, gk, gv), saved=True),
+                   max(3, args.steps // 5))
+        tt = timed(lambda: split.forward_train(q, k, v, out=ob, workspace=bws), max(3, args.steps // 5))
         out["backward"] = {"ms_per_call_p50": round(pct(tb, 0.5), 4),
-                           "tflops_at_2p5x_forward": round(2.5 * flops / (pct(tb, 0.5) * 1e-3) / 1e12, 2)}
+                           "tflops_at_2p5x_forward": round(2.5 * flops / (pct(tb, 0.5) * 1e-3) / 1e12, 2),
+                           "saved_state_ms_per_call_p50": round(pct(ts, 0.5), 4),
+                           "forward_train_ms_per_call_p50": round(pct(tt, 0.5), 4)}
         del bws, go, gq, gk, gv, ob
 
     # one frame-causal chunk (the last three frames against the cache of all earlier

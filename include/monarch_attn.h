@@ -44,7 +44,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 2
+#define MONARCH_ABI_VERSION 3
 
 typedef enum monarch_status {
   MONARCH_OK = 0,
@@ -185,6 +185,27 @@ size_t monarch_attn_backward_workspace_size(const monarch_plan* plan);
 monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, const void* k, const void* v,
                                      const void* o, const void* grad_o, void* grad_q, void* grad_k,
                                      void* grad_v, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Training forward: writes O = forward(Q, K, V) like monarch_attn_forward and leaves in
+ * `workspace` (a backward workspace: monarch_attn_backward_workspace_size bytes) the state the
+ * backward would otherwise recompute: the stage-1 output Y (bf16) and stage 1's per-row softmax
+ * statistics. The launches are those of the backward's recompute followed by stage 2, always the
+ * two-launch path with bf16 Y; for plans without MONARCH_FLAG_Y_FP32 and MONARCH_FLAG_FUSED, O
+ * is bitwise the output of monarch_attn_forward. bf16 plans with a backward only (else
+ * MONARCH_ERR_UNSUPPORTED); o must not overlap the inputs or the workspace, nor the workspace
+ * the inputs. Asynchronous on `stream`. */
+monarch_status monarch_attn_forward_train(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                          void* o, void* workspace, size_t workspace_bytes, void* stream);
+
+/* monarch_attn_backward without the forward recompute: `workspace` must hold the state a
+ * monarch_attn_forward_train call with the same plan, q, k and v left there, unchanged since
+ * (any other backward call on it overwrites that state). Arguments, checks, errors and outputs
+ * as monarch_attn_backward; with such a workspace the gradients are bitwise those of
+ * monarch_attn_backward. With any other workspace contents the call still returns MONARCH_OK
+ * and touches no memory outside its arguments, but the gradients are meaningless. */
+monarch_status monarch_attn_backward_saved(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                           const void* o, const void* grad_o, void* grad_q, void* grad_k,
+                                           void* grad_v, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* monarch_status_string(monarch_status status);

@@ -33,7 +33,7 @@ EXPORTED = [
     "monarch_attn_plan_info", "monarch_attn_forward", "monarch_attn_stage1",
     "monarch_attn_stage2", "monarch_status_string", "monarch_attn_kernel_name",
     "monarch_attn_abi_version", "monarch_attn_backward_workspace_size", "monarch_attn_backward",
-    "monarch_attn_chunk_forward",
+    "monarch_attn_chunk_forward", "monarch_attn_forward_train", "monarch_attn_backward_saved",
 ]
 
 
@@ -94,5 +94,9 @@ def lib() -> ctypes.CDLL:
     L.monarch_attn_backward.restype = i32
     L.monarch_attn_chunk_forward.argtypes = [vp, i32, i32, vp, vp, vp, vp, vp, vp]
     L.monarch_attn_chunk_forward.restype = i32
+    L.monarch_attn_forward_train.argtypes = [vp, vp, vp, vp, vp, vp, sz, vp]
+    L.monarch_attn_forward_train.restype = i32
+    L.monarch_attn_backward_saved.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.monarch_attn_backward_saved.restype = i32
     _lib = L
     return L

@@ -167,8 +167,29 @@ class MonarchPlan:
         """Workspace bytes of backward() (0: this plan has no backward)."""
         return int(_lib.lib().monarch_attn_backward_workspace_size(self._h))
 
-    def backward(self, q, k, v, o, grad_o, workspace=None, grads=None):
-        """(dL/dQ, dL/dK, dL/dV) for O = forward(q, k, v) and grad_o = dL/dO."""
+    def forward_train(self, q, k, v, out=None, workspace=None):
+        """(O, workspace): O = forward(q, k, v), and a backward workspace holding the state
+        backward(..., saved=True) uses instead of recomputing the forward."""
+        self._check_io(q, k, v)
+        if out is None:
+            out = torch.empty_like(q)
+        self._check_io(out)
+        n = self.backward_workspace_bytes
+        if workspace is None:
+            workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        ws_n = workspace.numel() * workspace.element_size()
+        st = _lib.lib().monarch_attn_forward_train(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                   out.data_ptr(), workspace.data_ptr(), ws_n, self._stream(q))
+        _check(st, "monarch_attn_forward_train")
+        return out, workspace
+
+    def backward(self, q, k, v, o, grad_o, workspace=None, grads=None, saved=False):
+        """(dL/dQ, dL/dK, dL/dV) for O = forward(q, k, v) and grad_o = dL/dO.
+
+        saved=True: `workspace` is the one forward_train(q, k, v) returned, unchanged since;
+        the forward is then not recomputed."""
+        if saved and workspace is None:
+            raise ValueError("saved=True needs the workspace forward_train returned")
         self._check_io(q, k, v, o, grad_o)
         for t in (q, k, v, o, grad_o):
             if t.dtype != self.dtype:
@@ -180,10 +201,11 @@ class MonarchPlan:
         if workspace is None:
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
         ws_n = workspace.numel() * workspace.element_size()
-        st = _lib.lib().monarch_attn_backward(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                                              grad_o.data_ptr(), grads[0].data_ptr(), grads[1].data_ptr(),
-                                              grads[2].data_ptr(), workspace.data_ptr(), ws_n, self._stream(q))
-        _check(st, "monarch_attn_backward")
+        fn = _lib.lib().monarch_attn_backward_saved if saved else _lib.lib().monarch_attn_backward
+        st = fn(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), grad_o.data_ptr(),
+                grads[0].data_ptr(), grads[1].data_ptr(), grads[2].data_ptr(), workspace.data_ptr(), ws_n,
+                self._stream(q))
+        _check(st, "monarch_attn_backward_saved" if saved else "monarch_attn_backward")
         return grads
 
     def close(self):

@@ -358,9 +358,42 @@ size_t monarch_attn_backward_workspace_size(const monarch_plan* plan) {
   return static_cast<size_t>(bwd_layout(plan->info).total);
 }
 
-monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, const void* k, const void* v,
-                                     const void* o, const void* grad_o, void* grad_q, void* grad_k, void* grad_v,
-                                     void* workspace, size_t workspace_bytes, void* stream) {
+// Training forward: the launches of the backward's forward recompute (stage 1
+// into the workspace's Y with its per-row statistics, bf16 Y), then stage 2
+// into O, so that a backward from the saved state skips the recompute.
+monarch_status monarch_attn_forward_train(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                          void* o, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!plan || !q || !k || !v || !o || !workspace) return MONARCH_ERR_INVALID_ARG;
+  const monarch_plan_info& p = plan->info;
+  if (!bwd_plan_ok(p)) return MONARCH_ERR_UNSUPPORTED;
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o) || misaligned(workspace))
+    return MONARCH_ERR_UNALIGNED;
+  const BwdLayout lay = bwd_layout(p);
+  if (static_cast<int64_t>(workspace_bytes) < lay.total) return MONARCH_ERR_WORKSPACE;
+  const int64_t io = tensor_bytes(p, p.dtype);
+  const void* ins[] = {q, k, v};
+  for (const void* x : ins)
+    if (overlap(o, io, x, io) || overlap(workspace, lay.total, x, io)) return MONARCH_ERR_ALIAS;
+  if (overlap(o, io, workspace, lay.total)) return MONARCH_ERR_ALIAS;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* w = static_cast<char*>(workspace);
+  void* y = w + lay.y;
+  const bool has1 = p.b > 1, has2 = p.m_tau > 1;
+  if (has1 || !has2) {
+    GroupedArgs f1 = stage1_args(p, q, k, v, has2 ? y : o, MONARCH_BF16);
+    f1.lse = reinterpret_cast<float*>(w + lay.lse1);
+    if (launch(choose_kernel(f1, p.flags), f1, s) != hipSuccess) return MONARCH_ERR_HIP;
+  }
+  if (has2) return run_stage2(p, q, k, has1 ? y : v, MONARCH_BF16, o, s);
+  return MONARCH_OK;
+}
+
+namespace {
+
+monarch_status backward_impl(const monarch_plan* plan, const void* q, const void* k, const void* v, const void* o,
+                             const void* grad_o, void* grad_q, void* grad_k, void* grad_v, void* workspace,
+                             size_t workspace_bytes, void* stream, bool saved) {
   if (!plan || !q || !k || !v || !o || !grad_o || !grad_q || !grad_k || !grad_v || !workspace)
     return MONARCH_ERR_INVALID_ARG;
   const monarch_plan_info& p = plan->info;
@@ -403,12 +436,13 @@ monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, co
   // stage-2 forward recompute, its backward and stage 1's delta
   const bool small2 = has1 && has2 && bwd_small_supported(stage2_args(p, q, k, y, MONARCH_BF16, nullptr));
 
-  // forward again, keeping Y and the per-row statistics
+  // forward again, keeping Y and the per-row statistics (or, from a training
+  // forward's saved state, only the argument set-up)
   GroupedArgs f1{}, f2{};
   if (has1 || !has2) {
     f1 = stage1_args(p, q, k, v, y, MONARCH_BF16);
     f1.lse = lse1;
-    if (!ok(launch(choose_kernel(f1, p.flags), f1, s))) return MONARCH_ERR_HIP;
+    if (!saved && !ok(launch(choose_kernel(f1, p.flags), f1, s))) return MONARCH_ERR_HIP;
   }
   if (small2) {
     BwdArgs b2{};
@@ -465,6 +499,20 @@ monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, co
     if (!ok(launch_bwd(b1, s))) return MONARCH_ERR_HIP;
   }
   return MONARCH_OK;
+}
+
+}  // namespace
+
+monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                     const void* o, const void* grad_o, void* grad_q, void* grad_k, void* grad_v,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(plan, q, k, v, o, grad_o, grad_q, grad_k, grad_v, workspace, workspace_bytes, stream, false);
+}
+
+monarch_status monarch_attn_backward_saved(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                           const void* o, const void* grad_o, void* grad_q, void* grad_k,
+                                           void* grad_v, void* workspace, size_t workspace_bytes, void* stream) {
+  return backward_impl(plan, q, k, v, o, grad_o, grad_q, grad_k, grad_v, workspace, workspace_bytes, stream, true);
 }
 
 const char* monarch_status_string(monarch_status status) {

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.monarch_attn_abi_version() == 2
+    assert L.monarch_attn_abi_version() == 3
 
 
 def _plan(batch=1, heads=2, d=128, grid=(4, 6, 10), align=0, custom_b=0, tile=0, dtype=0,
@@ -261,6 +261,50 @@ def test_backward_argument_errors():
     st, h = _plan(heads=2, grid=(4, 6, 10), dtype=1)
     assert L.monarch_attn_backward(h, *ptr[:8], ws, 1 << 30, None) == _lib.ERR_UNSUPPORTED
     L.monarch_attn_destroy(h)
+
+
+def test_backward_saved_argument_errors():
+    F = 1 << 36
+    st, h = _plan(heads=2, grid=(4, 6, 10))
+    n = L.monarch_attn_backward_workspace_size(h)
+    io = 2 * 240 * 128 * 2
+    ptr = [F + i * (1 << 30) for i in range(9)]
+    ws = F + 20 * (1 << 30)
+    call = lambda p, wsz=n, w=ws: L.monarch_attn_backward_saved(h, *p, w, wsz, None)
+    assert call([0] + ptr[1:8]) == _lib.ERR_INVALID_ARG
+    assert call(ptr[:8], w=0) == _lib.ERR_INVALID_ARG
+    assert call(ptr[:8], wsz=n - 1) == _lib.ERR_WORKSPACE
+    assert call([ptr[0] + 4] + ptr[1:8]) == _lib.ERR_UNALIGNED
+    assert call(ptr[:5] + [ptr[0] + 64] + ptr[6:8]) == _lib.ERR_ALIAS        # grad_q overlaps q
+    assert call(ptr[:8], w=ptr[7] + 32) == _lib.ERR_ALIAS                      # workspace overlaps grad_v
+    L.monarch_attn_destroy(h)
+    st, h = _plan(heads=2, grid=(4, 6, 10), dtype=1)
+    assert L.monarch_attn_backward_saved(h, *ptr[:8], ws, 1 << 30, None) == _lib.ERR_UNSUPPORTED
+    L.monarch_attn_destroy(h)
+
+
+def test_forward_train_argument_errors():
+    F = 1 << 36
+    st, h = _plan(heads=2, grid=(4, 6, 10))
+    n = L.monarch_attn_backward_workspace_size(h)
+    io = 2 * 240 * 128 * 2
+    q, k, v, o = (F + i * (1 << 30) for i in range(4))
+    ws = F + 20 * (1 << 30)
+    call = lambda *a, w=ws, wsz=n: L.monarch_attn_forward_train(h, *a, w, wsz, None)
+    assert call(0, k, v, o) == _lib.ERR_INVALID_ARG
+    assert call(q, k, v, 0) == _lib.ERR_INVALID_ARG
+    assert call(q, k, v, o, w=0) == _lib.ERR_INVALID_ARG
+    assert call(q, k, v, o, wsz=n - 1) == _lib.ERR_WORKSPACE
+    assert call(q, k + 8, v, o) == _lib.ERR_UNALIGNED
+    assert call(q, k, v, o, w=ws + 8) == _lib.ERR_UNALIGNED
+    assert call(q, k, v, v + io - 16) == _lib.ERR_ALIAS                      # o overlaps v
+    assert call(q, k, v, o, w=q + 256) == _lib.ERR_ALIAS                    # workspace overlaps q
+    assert call(q, k, v, ws + n - 16) == _lib.ERR_ALIAS                     # o overlaps the workspace
+    L.monarch_attn_destroy(h)
+    for kw in (dict(dtype=1), dict(flags=_lib.FLAG_GENERIC)):
+        st, h = _plan(heads=2, grid=(4, 6, 10), **kw)
+        assert L.monarch_attn_forward_train(h, q, k, v, o, ws, 1 << 30, None) == _lib.ERR_UNSUPPORTED
+        L.monarch_attn_destroy(h)
 
 
 # ------------------------------------------------------------------ chunk forward

@@ -89,3 +89,27 @@ def test_backward_full_size_two_heads(name):
     torch.cuda.synchronize()
     for x, y in zip(got, again):
         assert np.array_equal(x, to_np(y))
+
+
+SAVED = [SMALL[i] for i in (0, 1, 2, 5, 6, 8, 9)] + [((21, 30, 52), 128, "frame", 0, 0)]
+
+
+@pytest.mark.parametrize("grid,d,align,tile,cb", SAVED,
+                         ids=[f"{g[0]}x{g[1]}x{g[2]}-{a}-t{t}" for g, d, a, t, cb in SAVED])
+def test_forward_train_and_saved_backward_bitwise(grid, d, align, tile, cb):
+    # the training forward runs the backward's recompute launches: its O is
+    # bitwise the forward's, and the backward from its saved state is bitwise
+    # the recomputing backward (same kernels, same inputs)
+    heads = 2 if grid == (21, 30, 52) else 3
+    q, k, v = (x.to(DEV) for x in datagen.qkv(1, heads, grid, d, (71, 72, 73), dtype=BF16))
+    g = datagen.qkv(1, heads, grid, d, (74, 75, 76), dtype=BF16)[0].to(DEV)
+    plan = MonarchPlan(1, heads, d, grid, align=align, tile_tokens=tile, custom_b=cb)
+    o = plan.forward(q, k, v)
+    o_train, ws = plan.forward_train(q, k, v)
+    ref = plan.backward(q, k, v, o, g)
+    got = plan.backward(q, k, v, o_train, g, workspace=ws, saved=True)
+    torch.cuda.synchronize()
+    say(f"  {grid} {align} t{tile}: max |O_train - O| = {(o_train.float() - o.float()).abs().max().item():.1e}")
+    assert torch.equal(o_train, o)
+    for name, x, y in zip(("dQ", "dK", "dV"), got, ref):
+        assert torch.equal(x, y), name
