@@ -373,13 +373,12 @@ __device__ __forceinline__ float row_dot_acc(const f32x16 (&x)[D / 32], float mu
 }
 
 template <int D>
-__global__ void __launch_bounds__(64) bwd_small_kernel(BwdArgs b) {
+__global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
   constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * ROWB;
   __shared__ __attribute__((aligned(1024))) char qt[TILE];
   __shared__ __attribute__((aligned(1024))) char kt[TILE];
   __shared__ __attribute__((aligned(1024))) char vt[TILE];
   __shared__ __attribute__((aligned(1024))) char gt[TILE];
-  __shared__ float st_lse[32], st_del[32];
   const GroupedArgs& a = b.g;
   const int p = blockIdx.x % a.problems, hd = blockIdx.x / a.problems;
   const int64_t ntok = a.head_elems / D;
@@ -412,6 +411,10 @@ __global__ void __launch_bounds__(64) bwd_small_kernel(BwdArgs b) {
   __syncthreads();
   const FlashOffsets<D> fo(0, lane, rs);  // LDS read offsets of a tile's first 32 rows
 
+  // per-query statistics handed from (a) (lane = query) to (b) (register =
+  // query) by lane permutes, which need no LDS allocation: the four tiles
+  // alone (32 KB at d = 128) let five workgroups share a CU
+  float q_lse = 0.f, q_del = 0.f;
   // (a) lane = query r
   {
     bf16x8 qf[D / 16], gf[D / 16];
@@ -449,10 +452,8 @@ __global__ void __launch_bounds__(64) bwd_small_kernel(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) pd = fmaf(s[i], dp[i], pd);
     const float del = halves_sum(pd) * inv;
-    if (h == 0) {
-      st_lse[r] = mx + __builtin_amdgcn_logf(l);
-      st_del[r] = del;
-    }
+    q_lse = mx + __builtin_amdgcn_logf(l);
+    q_del = del;
 #pragma unroll
     for (int i = 0; i < 16; ++i) dp[i] = s[i] * inv * (dp[i] - del);
     f32x16 dq[D / 32];
@@ -466,7 +467,6 @@ __global__ void __launch_bounds__(64) bwd_small_kernel(BwdArgs b) {
     }
     store_rows<D>(rdq, true, rdq, false, r, rs, dq, c * 0.6931471805599453f, lane);
   }
-  __syncthreads();
 
   // (b) lane = key r
   {
@@ -485,29 +485,37 @@ __global__ void __launch_bounds__(64) bwd_small_kernel(BwdArgs b) {
     float lse[16], del[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      lse[i] = st_lse[acc_key(i, h)];
-      del[i] = st_del[acc_key(i, h)];
+      // lane acc_key(i, h) holds that query's values (both lane halves do)
+      const int src = 4 * acc_key(i, h);
+      lse[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(q_lse)));
+      del[i] = __int_as_float(__builtin_amdgcn_ds_bpermute(src, __float_as_int(q_del)));
     }
     probs_grads(s, dp, lse, del, c);
-    f32x16 dv[D / 32], dk[D / 32];
+    const bf16x8 pp[2] = {p_operand(s, 0), p_operand(s, 1)};
+    const bf16x8 ps[2] = {p_operand(dp, 0), p_operand(dp, 1)};
+    // dV, then dK: one 64-register accumulator at a time (two waves per SIMD)
+    {
+      f32x16 dv[D / 32];
 #pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) {
-      dv[mt] = f32x16{};
-      dk[mt] = f32x16{};
+      for (int mt = 0; mt < D / 32; ++mt) dv[mt] = f32x16{};
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dv[mt] = mma(v_operand<D>(gt, fo, mt, st), pp[st], dv[mt]);
+      store_rows<D>(rdv, false, rdv, false, r, rs, dv, 1.f, lane);
+      const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, r, h));
+      if (h == 0 && r < L) b.dv_delta[hd * ntok + base + r * rs] = d1;
     }
+    {
+      f32x16 dk[D / 32];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const bf16x8 pp = p_operand(s, st), ps = p_operand(dp, st);
+      for (int mt = 0; mt < D / 32; ++mt) dk[mt] = f32x16{};
 #pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        dv[mt] = mma(v_operand<D>(gt, fo, mt, st), pp, dv[mt]);
-        dk[mt] = mma(v_operand<D>(qt, fo, mt, st), ps, dk[mt]);
-      }
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dk[mt] = mma(v_operand<D>(qt, fo, mt, st), ps[st], dk[mt]);
+      store_rows<D>(rdk, true, rdk, false, r, rs, dk, c * 0.6931471805599453f, lane);
     }
-    store_rows<D>(rdk, true, rdk, false, r, rs, dk, c * 0.6931471805599453f, lane);
-    store_rows<D>(rdv, false, rdv, false, r, rs, dv, 1.f, lane);
-    const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, r, h));
-    if (h == 0 && r < L) b.dv_delta[hd * ntok + base + r * rs] = d1;
   }
 }
 

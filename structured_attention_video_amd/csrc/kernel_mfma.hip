@@ -321,10 +321,13 @@ struct GroupCfg {
   static constexpr int tile = BN * ROWB;
   static constexpr int RPI = 1024 / ROWB;  // rows per DMA instruction
   static constexpr int IPW = 32 / RPI;     // DMA instructions per wave per tile
+  // waves per SIMD the register budget aims at: two unless the three tiles
+  // already keep a second workgroup off the CU (128-row tiles at d = 128)
+  static constexpr int MINW = 3 * tile <= 80 * 1024 ? 2 : 1;
 };
 
 template <int D, int QT, bool OUT_F32>
-__global__ void __launch_bounds__((GroupCfg<D, QT>::NT), 2) group_kernel(GroupedArgs a) {
+__global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)) group_kernel(GroupedArgs a) {
   using G = GroupCfg<D, QT>;
   __shared__ __attribute__((aligned(1024))) char ql[G::tile];
   __shared__ __attribute__((aligned(1024))) char kl[G::tile];
