@@ -282,7 +282,38 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
   if (a.lse && h == 0 && row0 + (lane & 31) < Lq)
     a.lse[hd * (a.head_elems / D) + qbase + (row0 + (lane & 31)) * rs] = st.m + __builtin_amdgcn_logf(lsum);
-  store_out<D, OUT_F32, POLICY>(ro, row0 + (lane & 31), rs, st.o, 1.f / lsum, lane);
+  if constexpr (OUT_F32) {
+    store_out<D, true, POLICY>(ro, row0 + (lane & 31), rs, st.o, 1.f / lsum, lane);
+  } else {
+    // Stage this wave's 32 rows in its own half of a K slot (no wave reads K
+    // after the loop), swizzled, then store whole rows (16-byte pieces of
+    // 256-byte rows, four rows per instruction) instead of 8-byte pieces of 32
+    // rows. Only this wave touches its half: the LDS ops of one wave run in
+    // order, the wait and the wave barrier keep the compiler from moving the
+    // reads above the writes.
+    constexpr int ROWB = D * 2, CPR = D / 8, RPI = 64 / CPR;
+    char* stage = (wave < 2 ? k0 : k1) + (wave & 1) * 32 * ROWB;
+    const int r = lane & 31;
+    const float inv = 1.f / lsum;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(st.o[mt][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(stage + swoff<D>(r, 4 * mt + g) + 8 * h) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = RPI * i + lane / CPR, chk = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + swoff<D>(rr, chk));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(((row0 + rr) * rs * D + chk * 8) * 2), 0,
+                                             POLICY);
+    }
+  }
 }
 
 // Waves per workgroup of the flash kernel: four (two workgroups per CU).
