@@ -280,10 +280,14 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
-  if (a.lse && h == 0 && row0 + (lane & 31) < Lq)
-    a.lse[hd * (a.head_elems / D) + qbase + (row0 + (lane & 31)) * rs] = st.m + __builtin_amdgcn_logf(lsum);
+  // lane-derived indices made opaque here, so that no address below is
+  // computed before the loop and kept live across it (that spilled)
+  int r = lane & 31;
+  asm volatile("" : "+v"(r));
+  if (a.lse && h == 0 && row0 + r < Lq)
+    a.lse[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = st.m + __builtin_amdgcn_logf(lsum);
   if constexpr (OUT_F32) {
-    store_out<D, true, POLICY>(ro, row0 + (lane & 31), rs, st.o, 1.f / lsum, lane);
+    store_out<D, true, POLICY>(ro, row0 + r, rs, st.o, 1.f / lsum, lane);
   } else {
     // Stage this wave's 32 rows in its own half of a K slot (no wave reads K
     // after the loop), swizzled, then store whole rows (16-byte pieces of
@@ -293,7 +297,8 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
     // reads above the writes.
     constexpr int ROWB = D * 2, CPR = D / 8, RPI = 64 / CPR;
     char* stage = (wave < 2 ? k0 : k1) + (wave & 1) * 32 * ROWB;
-    const int r = lane & 31;
+    int lr = lane / CPR;
+    asm volatile("" : "+v"(lr));
     const float inv = 1.f / lsum;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
@@ -306,12 +311,13 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
       }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
+    const uint32_t row_bytes = static_cast<uint32_t>(rs * D * 2);  // offsets fit 32 bits (offsets_fit)
 #pragma unroll
     for (int i = 0; i < 32 / RPI; ++i) {
-      const int rr = RPI * i + lane / CPR, chk = lane % CPR;
+      const int rr = RPI * i + lr, chk = lane % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + swoff<D>(rr, chk));
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(((row0 + rr) * rs * D + chk * 8) * 2), 0,
-                                             POLICY);
+      const uint32_t off = static_cast<uint32_t>(row0 + rr) * row_bytes + static_cast<uint32_t>(chk * 16);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(off), 0, POLICY);
     }
   }
 }
