@@ -372,6 +372,68 @@ __device__ __forceinline__ float row_dot_acc(const f32x16 (&x)[D / 32], float mu
   return acc;
 }
 
+// One wave stores its 32 rows of x^T accumulators (lane: row lane % 32,
+// channels 32 mt + 8 (i / 4) + 4 h + i % 4), scaled by mul, as whole rows
+// through LDS: written into the wave's dead tiles, read back 16 bytes per lane
+// (fp32 rows: two or four per instruction; bf16 rows: four or eight), stored
+// with one instruction per 1 KB. fp32 rows go to t0 (rows 0..15) and t1
+// (rows 16..31), 16-byte chunk c of row r at c ^ (r % 16); bf16 rows to t0
+// in the tile swizzle. Rows past the problem's end are dropped by ro.
+template <int D, bool F32>
+__device__ __forceinline__ void stage_rows(char* t0, char* t1, const f32x16 (&x)[D / 32], float mul,
+                                           __amdgpu_buffer_rsrc_t ro, int64_t rs, int lane) {
+  const int h = lane >> 5;
+  int r = lane & 31;
+  asm volatile("" : "+v"(r));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier reads of the tiles are done
+  __builtin_amdgcn_wave_barrier();
+  if constexpr (F32) {
+    constexpr int RB = D * 4, CH = D / 4, RPI = 64 / CH;
+    char* t = r < 16 ? t0 : t1;
+    const int rr = r & 15;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x4 v = {__float_as_uint(x[mt][4 * g] * mul), __float_as_uint(x[mt][4 * g + 1] * mul),
+                         __float_as_uint(x[mt][4 * g + 2] * mul), __float_as_uint(x[mt][4 * g + 3] * mul)};
+        *reinterpret_cast<u32x4*>(t + rr * RB + 16 * ((8 * mt + 2 * g + h) ^ rr)) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t row_bytes = static_cast<uint32_t>(rs * D * 4);
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + lane / CH, chk = lane % CH;
+      const char* tr = row < 16 ? t0 : t1;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(tr + (row & 15) * RB + 16 * (chk ^ (row & 15)));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(row * row_bytes + chk * 16), 0, 0);
+    }
+  } else {
+    constexpr int CPR = D / 8, RPI = 64 / CPR;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(x[mt][4 * g + e] * mul);
+        *reinterpret_cast<bf16x4*>(t0 + swoff<D>(r, 4 * mt + g) + 8 * h) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    const uint32_t row_bytes = static_cast<uint32_t>(rs * D * 2);
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int row = RPI * i + lane / CPR, chk = lane % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(t0 + swoff<D>(row, chk));
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(row * row_bytes + chk * 16), 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // the read-backs are done before the tiles are reused
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int D>
 __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
   constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * ROWB;
@@ -415,6 +477,7 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
   // query) by lane permutes, which need no LDS allocation: the four tiles
   // alone (32 KB at d = 128) let five workgroups share a CU
   float q_lse = 0.f, q_del = 0.f;
+  bf16x8 dsb[2];
   // (a) lane = query r
   {
     bf16x8 qf[D / 16], gf[D / 16];
@@ -456,16 +519,10 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
     q_del = del;
 #pragma unroll
     for (int i = 0; i < 16; ++i) dp[i] = s[i] * inv * (dp[i] - del);
-    f32x16 dq[D / 32];
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const bf16x8 pb = p_operand(dp, st);
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mma(v_operand<D>(kt, fo, mt, st), pb, dq[mt]);
-    }
-    store_rows<D>(rdq, true, rdq, false, r, rs, dq, c * 0.6931471805599453f, lane);
+    // dS^T as bf16 operands: dQ^T = K^T dS^T comes last, once the other
+    // tiles are free to stage the outputs
+    dsb[0] = p_operand(dp, 0);
+    dsb[1] = p_operand(dp, 1);
   }
 
   // (b) lane = key r
@@ -502,9 +559,9 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) dv[mt] = mma(v_operand<D>(gt, fo, mt, st), pp[st], dv[mt]);
-      store_rows<D>(rdv, false, rdv, false, r, rs, dv, 1.f, lane);
       const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, r, h));
       if (h == 0 && r < L) b.dv_delta[hd * ntok + base + r * rs] = d1;
+      stage_rows<D, false>(vt, vt, dv, 1.f, rdv, rs, lane);  // V and G are dead now
     }
     {
       f32x16 dk[D / 32];
@@ -514,8 +571,20 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
       for (int st = 0; st < 2; ++st)
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) dk[mt] = mma(v_operand<D>(qt, fo, mt, st), ps[st], dk[mt]);
-      store_rows<D>(rdk, true, rdk, false, r, rs, dk, c * 0.6931471805599453f, lane);
+      stage_rows<D, true>(gt, vt, dk, c * 0.6931471805599453f, rdk, rs, lane);
     }
+  }
+
+  // (a, end) dQ^T = K^T dS^T, lane = query r
+  {
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mma(v_operand<D>(kt, fo, mt, st), dsb[st], dq[mt]);
+    stage_rows<D, true>(qt, gt, dq, c * 0.6931471805599453f, rdq, rs, lane);
   }
 }
 
