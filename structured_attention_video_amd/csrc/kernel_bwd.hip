@@ -588,24 +588,43 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
   }
 }
 
-template <int D>
-__global__ void __launch_bounds__(256) rowdot_kernel(const void* a, int ta, const void* bp, int tb, float* out,
-                                                     int64_t rows) {
-  // D/8 lanes per row, 8 channels each, reduced across the row's lanes
+// 8 consecutive elements of a row as floats (one 16-byte load for bf16, two
+// for fp32)
+template <bool F32>
+__device__ __forceinline__ void load8(const void* base, int64_t e0, float (&x)[8]) {
+  if constexpr (F32) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + e0);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(static_cast<const float*>(base) + e0 + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = __uint_as_float(a[e]);
+      x[4 + e] = __uint_as_float(b[e]);
+    }
+  } else {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(base) + e0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = __uint_as_float(a[e] << 16);
+      x[2 * e + 1] = __uint_as_float(a[e] & 0xffff0000u);
+    }
+  }
+}
+
+// out[row] = sum over the D channels of a[row] * b[row]: D/8 lanes per row,
+// 8 channels each (16-byte loads), reduced across the row's lanes
+template <int D, bool FA, bool FB>
+__global__ void __launch_bounds__(256) rowdot_kernel(const void* a, const void* bp, float* out, int64_t rows) {
   constexpr int LP = D / 8;
   const int64_t row = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) / LP;
   const int sub = threadIdx.x % LP;
   const int64_t rr = row < rows ? row : rows - 1;
-  float acc = 0.f;
   const int64_t e0 = rr * D + sub * 8;
+  float x[8], y[8];
+  load8<FA>(a, e0, x);
+  load8<FB>(bp, e0, y);
+  float acc = 0.f;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = ta == kF32 ? static_cast<const float*>(a)[e0 + e]
-                               : static_cast<float>(static_cast<const bf16*>(a)[e0 + e]);
-    const float y = tb == kF32 ? static_cast<const float*>(bp)[e0 + e]
-                               : static_cast<float>(static_cast<const bf16*>(bp)[e0 + e]);
-    acc = fmaf(x, y, acc);
-  }
+  for (int e = 0; e < 8; ++e) acc = fmaf(x[e], y[e], acc);
 #pragma unroll
   for (int off = LP / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, LP);
   if (sub == 0 && row < rows) out[row] = acc;
@@ -661,12 +680,17 @@ hipError_t launch_rowdot(const void* a, ElemType ta, const void* bp, ElemType tb
   const int64_t threads = rows * (D / 8);
   const int64_t grid = (threads + 255) / 256;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (D == 128)
-    hipLaunchKernelGGL(rowdot_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a, ta, bp, tb, out,
-                       rows);
-  else
-    hipLaunchKernelGGL(rowdot_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s, a, ta, bp, tb, out,
-                       rows);
+  const dim3 g(static_cast<unsigned>(grid)), blk(256);
+  const bool fa = ta == kF32, fb = tb == kF32;
+#define MONARCH_ROWDOT(DD, A, B) hipLaunchKernelGGL((rowdot_kernel<DD, A, B>), g, blk, 0, s, a, bp, out, rows)
+  if (D == 128) {
+    if (fa) { if (fb) MONARCH_ROWDOT(128, true, true); else MONARCH_ROWDOT(128, true, false); }
+    else { if (fb) MONARCH_ROWDOT(128, false, true); else MONARCH_ROWDOT(128, false, false); }
+  } else {
+    if (fa) { if (fb) MONARCH_ROWDOT(64, true, true); else MONARCH_ROWDOT(64, true, false); }
+    else { if (fb) MONARCH_ROWDOT(64, false, true); else MONARCH_ROWDOT(64, false, false); }
+  }
+#undef MONARCH_ROWDOT
   return hipGetLastError();
 }
 
