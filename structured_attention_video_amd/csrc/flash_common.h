@@ -23,33 +23,6 @@ __device__ __forceinline__ int xcd_order(int w, int nwg) {
   return x < r ? x * (q + 1) + slot : r * (q + 1) + (x - r) * q + slot;
 }
 
-// Per-thread byte offsets of the 16-byte chunks a cooperative tile load
-// covers: chunk id = tid + NT*c -> row id/CPR, channels 8*(id%CPR).. (16
-// consecutive lanes read one 256-byte row).
-template <int D, int ROWS, int NT>
-struct TileOffsets {
-  static constexpr int CPR = D / 8;
-  static constexpr int N = ROWS * CPR / NT;
-  uint32_t g[N];  // global, relative to row 0 of the tile
-  uint32_t s[N];  // LDS
-  __device__ __forceinline__ TileOffsets(int tid, int64_t rs) {
-#pragma unroll
-    for (int c = 0; c < N; ++c) {
-      const int id = tid + NT * c;
-      g[c] = static_cast<uint32_t>(((id / CPR) * rs * D + (id % CPR) * 8) * 2);
-      s[c] = static_cast<uint32_t>((id / CPR) * KRow<D>::bytes + (id % CPR) * 16);
-    }
-  }
-  __device__ __forceinline__ void load(u32x4* r, __amdgpu_buffer_rsrc_t src, uint32_t tile_off) const {
-#pragma unroll
-    for (int c = 0; c < N; ++c) r[c] = bload16(src, g[c] + tile_off);
-  }
-  __device__ __forceinline__ void store(char* lds, const u32x4* r) const {
-#pragma unroll
-    for (int c = 0; c < N; ++c) *reinterpret_cast<u32x4*>(lds + s[c]) = r[c];
-  }
-};
-
 // ---------------------------------------------------------------- flash
 constexpr int FBM = 128;  // query rows per four-wave workgroup
 constexpr int FBN = 64;   // keys per LDS tile

@@ -58,17 +58,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // key index of accumulator register i for lane half h, in a 32-key tile
 __device__ __forceinline__ int acc_key(int i, int h) { return 8 * (i >> 2) + 4 * h + (i & 3); }
 
-// LDS rows of K and V (channels contiguous) are padded by 32 bytes: the 8
-// rows of a 16-byte read phase, and the 4 rows x 4 segments of a transposing
-// read, start in distinct banks. (48 bytes also clears the 16-row phase and
-// halves the measured conflict cycles, but measured slower: 77.8 KB of LDS
-// per workgroup leaves almost none spare with two workgroups per CU.)
-#ifndef MONARCH_ROW_PAD
-#define MONARCH_ROW_PAD 32
-#endif
-template <int D>
-struct KRow { static constexpr int bytes = D * 2 + MONARCH_ROW_PAD; };
-
 __device__ __forceinline__ bf16x8 ld_bf16x8(const char* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // ---------------------------------------------------------------- global access
@@ -103,40 +92,6 @@ __device__ __forceinline__ void load_qfrag(bf16x8 (&qf)[D / 16], __amdgpu_buffer
 }
 
 // ---------------------------------------------------------------- matrix products
-// S^T for one 32-key tile of K in LDS (rows key0..key0+31) against a wave's
-// query fragment qf.
-template <int D>
-__device__ __forceinline__ f32x16 scores_tile(const char* kl, int key0, const bf16x8 (&qf)[D / 16], int lane) {
-  constexpr int KR = KRow<D>::bytes;
-  const char* row = kl + (key0 + (lane & 31)) * KR + (lane >> 5) * 16;
-  f32x16 s = {};
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) s = mma(ld_bf16x8(row + ks * 32), qf[ks], s);
-  return s;
-}
-
-// V^T A operand for channels 32*mt .. +32 and the 16-key step `step` of a
-// row-major V tile in LDS: lane half h element e holds key
-// 16*step + 8*(e/4) + 4*h + e%4 (two transposing reads, keys +0..3 / +8..11).
-template <int D>
-__device__ __forceinline__ bf16x8 vt_operand(const char* vl, int mt, int step, int lane) {
-  constexpr int R = KRow<D>::bytes;
-  const int j = lane & 15, g = lane >> 4;
-  const int key = 16 * step + 4 * (g >> 1) + (j >> 2);
-  const int ch = 32 * mt + 16 * (g & 1) + 4 * (j & 3);
-  const char* p = vl + key * R + ch * 2;
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * R));
-  const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// O^T[32*mt .. +32) += V^T P^T over one 16-key step
-template <int D>
-__device__ __forceinline__ f32x16 pv_step(const char* vl, int mt, int step, bf16x8 p, f32x16 o, int lane) {
-  return mma(vt_operand<D>(vl, mt, step, lane), p, o);
-}
-
 // bf16 B operand for PV step `step` from probabilities held as accumulator
 // tiles (registers 8*(step%2) .. +7 of tile step/2)
 __device__ __forceinline__ bf16x8 p_operand(const f32x16& p, int half) {
