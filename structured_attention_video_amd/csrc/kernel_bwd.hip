@@ -190,7 +190,10 @@ __device__ __forceinline__ bf16x8 bias_ones(int h) {
 }
 
 // MODE 0: dV only (S -> P; dV^T += G^T P). MODE 1: dK only (S, dP -> dS;
-// dK^T += Q^T dS). In MODE 1 the per-query lse and delta enter the products
+// dK^T += Q^T dS). MODE 1 raises the wave's priority over its matrix-product
+// phases (s_setprio 1), so the two waves sharing a SIMD tend to alternate
+// between products and exponentials (measured -4.5% at the frame shape; the
+// same change slowed bwd_dq by as much and left MODE 0 unchanged). In MODE 1 the per-query lse and delta enter the products
 // as a bias K-step (c S - lse and dP - delta come out of the accumulators),
 // so a lane needs only its own query's two values, not one per accumulator
 // register: without it the kernel spilled 25 VGPRs (measured 693 -> 628 us at
@@ -276,6 +279,7 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
       // S = Q K^T, dP = G V^T for 32 queries: lane = key, register i = query
       // 32*sub + 8*(i/4) + 4*h + i%4 of the tile
       f32x16 s = {}, dp = {};
+      if (MODE == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         s = mma(k_operand<D>(qc, fo, ks, sub), kf[ks], s);
@@ -286,6 +290,7 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
         const int qrow = 32 * sub + (lane & 31);
         s = mma(bias_operand(-st_lse[sc][qrow] * inv_c, h), ones, s);
         dp = mma(bias_operand(-st_del[sc][qrow], h), ones, dp);
+        __builtin_amdgcn_s_setprio(0);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           s[i] = fast_exp2(s[i] * c);  // P
@@ -306,6 +311,7 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
         probs_grads(s, dp, lse, del, c);
       }
       // dV^T += G^T P (MODE 0) or dK^T += Q^T dS (MODE 1), two 16-query steps
+      if (MODE == 1) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const bf16x8 pb = p_operand(MODE == 1 ? dp : s, st);
@@ -313,6 +319,7 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
         for (int mt = 0; mt < D / 32; ++mt)
           acc[mt] = mma(v_operand<D>(MODE == 1 ? qc : gc, fo, mt, 2 * sub + st), pb, acc[mt]);
       }
+      if (MODE == 1) __builtin_amdgcn_s_setprio(0);
     }
     if (j + 1 < n) stats_store(sc ^ 1);
     wait_dma();

@@ -648,7 +648,8 @@ bool offsets_fit(const GroupedArgs& a, int pad_rows) {
 template <int D, bool F32>
 hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   // query rows in units of one wave's 32, spread evenly over the fewest
-  // tiles of at most kFlashWaves units (a 1560-row block: 7 tiles of 224)
+  // tiles of at most kFlashWaves units (a 1560-row block: 49 units, 13 tiles
+  // of 128 rows, the last holding 24)
   const int units = (a.Lq + 31) / 32;
   if (units <= 0) return hipErrorInvalidConfiguration;
   const int qtiles = (units + kFlashWaves - 1) / kFlashWaves;
