@@ -73,6 +73,10 @@ hipError_t launch_bwd(const BwdArgs& b, hipStream_t stream);
 // dv, dv_delta; lse, delta, dq_in and dk_in are not used.
 bool bwd_small_supported(const GroupedArgs& g);
 hipError_t launch_bwd_small(const BwdArgs& b, hipStream_t stream);
+// The same for problems of 33..128 rows (the long layout's stage-2 groups): one
+// workgroup of ceil(L / 32) waves per problem; same arguments and outputs.
+bool bwd_group_supported(const GroupedArgs& g);
+hipError_t launch_bwd_group(const BwdArgs& b, hipStream_t stream);
 // out[r] = sum_c a[r][c] * b[r][c] over rows x D (bf16 or fp32 elements)
 hipError_t launch_rowdot(const void* a, ElemType ta, const void* b, ElemType tb, float* out, int64_t rows, int D,
                          hipStream_t stream);

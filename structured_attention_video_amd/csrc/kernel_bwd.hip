@@ -595,6 +595,182 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
   }
 }
 
+// ---------------------------------------------------------------- mid-size problems, one pass
+// One workgroup of W = ceil(L / 32) waves per problem of 33..128 rows (the
+// long layout's stage-2 groups, m = 81), the multi-wave form of
+// bwd_small_kernel with the same inputs and outputs. Q, K, V (the stage's
+// values) and G rows are copied whole into four swizzled 32W-row LDS tiles;
+// wave w owns rows 32w .. 32w+31.
+//   (a) lane = query: S^T and dP^T against every 32-key block, the row max,
+//       sum, lse and delta = sum over keys of P dP (fp32, in registers),
+//       dS^T as bf16 operands, and dQ^T = K^T dS^T, kept in registers; lse
+//       and delta of each query go to LDS;
+//   (b) lane = key: S and dP against every 32-query block with lse and delta
+//       read per register, dV^T = G^T P and dK^T = Q^T dS in one sweep, and
+//       the next stage's delta of each key row, rowsum(dV * V) with dV
+//       rounded as stored.
+// The tiles (up to 128 KB at d = 128) leave room for one workgroup per CU,
+// so each wave has a SIMD to itself and the register budget of a lone wave:
+// the three accumulators need not take turns. Outputs leave as whole rows
+// through the tiles once every wave is done with them.
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W, 1) bwd_group_kernel(BwdArgs b) {
+  constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * W * ROWB;
+  __shared__ __attribute__((aligned(1024))) char qt[TILE];
+  __shared__ __attribute__((aligned(1024))) char kt[TILE];
+  __shared__ __attribute__((aligned(1024))) char vt[TILE];
+  __shared__ __attribute__((aligned(1024))) char gt[TILE];
+  __shared__ __attribute__((aligned(16))) float xl[32 * W];
+  __shared__ __attribute__((aligned(16))) float xd[32 * W];
+  const GroupedArgs& a = b.g;
+  const int p = blockIdx.x % a.problems, hd = blockIdx.x / a.problems;
+  const int64_t ntok = a.head_elems / D;
+  const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
+  const int64_t base = problem_base(a, p);
+  const int64_t rs = a.row_stride;
+  const int L = a.L;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int own = 32 * wave;  // first row of this wave
+  const float c = a.scale_log2;
+  {
+    const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+    const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
+    const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
+    const auto rg = problem_rsrc(static_cast<const bf16*>(b.go) + hoff, base, rs, L, D, 2);
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = own + RPI * i + lane / CPR;
+      const int ch = (lane % CPR) ^ swz<D>(row);
+      const uint32_t goff = static_cast<uint32_t>((row * rs * D + ch * 8) * 2);
+      const int dst = (own + RPI * i) * ROWB;
+      lds_dma16(rq, qt + dst, goff);
+      lds_dma16(rk, kt + dst, goff);
+      lds_dma16(rv, vt + dst, goff);
+      lds_dma16(rg, gt + dst, goff);
+    }
+  }
+  wait_dma();
+  __syncthreads();
+  const FlashOffsets<D> fo(0, lane, rs);  // LDS read offsets of a 32-row block
+
+  // (a) lane = query own + r
+  f32x16 dq[D / 32];
+  {
+    bf16x8 qf[D / 16], gf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = ld_bf16x8(qt + swoff<D>(own + r, 2 * ks + h));
+      gf[ks] = ld_bf16x8(gt + swoff<D>(own + r, 2 * ks + h));
+    }
+    f32x16 s[W], dp[W];
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s[kb] = mma(k_operand<D>(kt, fo, ks, kb), qf[ks], s[kb]);
+        dp[kb] = mma(k_operand<D>(vt, fo, ks, kb), gf[ks], dp[kb]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (32 * kb + acc_key(i, h) >= L) s[kb][i] = -INFINITY;
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = halves_max(mx) * c;
+    float l = 0.f, pd = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -mx));
+        l += s[kb][i];
+        pd = fmaf(s[kb][i], dp[kb][i], pd);
+      }
+    l = halves_sum(l);
+    const float inv = 1.f / l;
+    // delta from the fp32 P and dP in registers (as bwd_small_kernel)
+    const float del = halves_sum(pd) * inv;
+    if (h == 0) {
+      xl[own + r] = mx + __builtin_amdgcn_logf(l);
+      xd[own + r] = del;
+    }
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[kb][i] = s[kb][i] * inv * (dp[kb][i] - del);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 ds = p_operand(dp[kb], st);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mma(v_operand<D>(kt, fo, mt, 2 * kb + st), ds, dq[mt]);
+      }
+    }
+  }
+  __syncthreads();  // lse and delta of every query are in LDS
+
+  // (b) lane = key own + r
+  f32x16 dv[D / 32], dk[D / 32];
+  {
+    bf16x8 kf[D / 16], vf[D / 16];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = ld_bf16x8(kt + swoff<D>(own + r, 2 * ks + h));
+      vf[ks] = ld_bf16x8(vt + swoff<D>(own + r, 2 * ks + h));
+    }
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) {
+      dv[mt] = f32x16{};
+      dk[mt] = f32x16{};
+    }
+#pragma unroll
+    for (int qb = 0; qb < W; ++qb) {
+      f32x16 s = {}, dp = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s = mma(k_operand<D>(qt, fo, ks, qb), kf[ks], s);
+        dp = mma(k_operand<D>(gt, fo, ks, qb), vf[ks], dp);
+      }
+      float lse[16], del[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        lse[i] = xl[32 * qb + acc_key(i, h)];
+        del[i] = xd[32 * qb + acc_key(i, h)];
+      }
+      probs_grads(s, dp, lse, del, c);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 pp = p_operand(s, st), ps = p_operand(dp, st);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+          dv[mt] = mma(v_operand<D>(gt, fo, mt, 2 * qb + st), pp, dv[mt]);
+          dk[mt] = mma(v_operand<D>(qt, fo, mt, 2 * qb + st), ps, dk[mt]);
+        }
+      }
+    }
+    const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, own + r, h));
+    if (h == 0 && own + r < L) b.dv_delta[hd * ntok + base + (own + r) * rs] = d1;
+  }
+  __syncthreads();  // every wave is done with every tile
+
+  // this wave's rows leave through its own rows of the (now dead) tiles
+  const int64_t wbase = base + own * rs;
+  const int wl = L - own;  // >= 1: W = ceil(L / 32)
+  const auto rdv = problem_rsrc(static_cast<const char*>(b.dv) + hoff * 2, wbase, rs, wl, D, 2);
+  stage_rows<D, false>(qt + own * ROWB, qt + own * ROWB, dv, 1.f, rdv, rs, lane);
+  const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * 4, wbase, rs, wl, D, 4);
+  stage_rows<D, true>(kt + own * ROWB, vt + own * ROWB, dk, c * 0.6931471805599453f, rdk, rs, lane);
+  const auto rdq = problem_rsrc(static_cast<const char*>(b.dq) + hoff * 4, wbase, rs, wl, D, 4);
+  stage_rows<D, true>(gt + own * ROWB, qt + own * ROWB, dq, c * 0.6931471805599453f, rdq, rs, lane);
+}
+
 // 8 consecutive elements of a row as floats (one 16-byte load for bf16, two
 // for fp32)
 template <bool F32>
@@ -678,6 +854,28 @@ hipError_t launch_bwd_small(const BwdArgs& b, hipStream_t s) {
     hipLaunchKernelGGL(bwd_small_kernel<128>, dim3(static_cast<unsigned>(nwg)), dim3(64), 0, s, b);
   else
     hipLaunchKernelGGL(bwd_small_kernel<64>, dim3(static_cast<unsigned>(nwg)), dim3(64), 0, s, b);
+  return hipGetLastError();
+}
+
+bool bwd_group_supported(const GroupedArgs& g) {
+  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L > 32 && g.L <= 128 &&
+         g.q_row0 == 0 && g.Lq == g.L && (static_cast<int64_t>(128) + 32) * g.row_stride * g.D * 4 < (int64_t{1} << 31);
+}
+
+hipError_t launch_bwd_group(const BwdArgs& b, hipStream_t s) {
+  const GroupedArgs& g = b.g;
+  if (!bwd_group_supported(g) || !b.go || !b.dq || !b.dk || !b.dv || !b.dv_delta) return hipErrorInvalidValue;
+  const int64_t nwg = static_cast<int64_t>(g.problems) * g.heads;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(nwg));
+  const int w = (g.L + 31) / 32;
+#define MONARCH_BWD_GROUP(DD, WW) hipLaunchKernelGGL((bwd_group_kernel<DD, WW>), grid, dim3(64 * WW), 0, s, b)
+  if (g.D == 128) {
+    if (w == 2) MONARCH_BWD_GROUP(128, 2); else if (w == 3) MONARCH_BWD_GROUP(128, 3); else MONARCH_BWD_GROUP(128, 4);
+  } else {
+    if (w == 2) MONARCH_BWD_GROUP(64, 2); else if (w == 3) MONARCH_BWD_GROUP(64, 3); else MONARCH_BWD_GROUP(64, 4);
+  }
+#undef MONARCH_BWD_GROUP
   return hipGetLastError();
 }
 

@@ -432,9 +432,12 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
   const int D = static_cast<int>(p.head_dim);
   const bool has1 = p.b > 1, has2 = p.m_tau > 1;
   auto ok = [](hipError_t e) { return e == hipSuccess; };
-  // stage-2 problems of at most 32 rows (frame layout): one launch does the
-  // stage-2 forward recompute, its backward and stage 1's delta
-  const bool small2 = has1 && has2 && bwd_small_supported(stage2_args(p, q, k, y, MONARCH_BF16, nullptr));
+  // stage-2 problems of at most 128 rows (frame and long layouts): one launch
+  // does the stage-2 forward recompute, its backward and stage 1's delta
+  const GroupedArgs g2 = stage2_args(p, q, k, y, MONARCH_BF16, nullptr);
+  const bool one32 = has1 && has2 && bwd_small_supported(g2);
+  const bool one128 = has1 && has2 && !one32 && bwd_group_supported(g2);
+  const bool small2 = one32 || one128;
 
   // forward again, keeping Y and the per-row statistics (or, from a training
   // forward's saved state, only the argument set-up)
@@ -452,7 +455,7 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
     b2.dk = dk2; b2.dk_type = kF32;
     b2.dv = dy; b2.dv_type = kBF16;
     b2.dv_delta = del1;
-    if (!ok(launch_bwd_small(b2, s))) return MONARCH_ERR_HIP;
+    if (!ok(one32 ? launch_bwd_small(b2, s) : launch_bwd_group(b2, s))) return MONARCH_ERR_HIP;
   }
   if (has2 && !small2) {
     // values: Y (or V when stage 1 is the identity). The recomputed output is

@@ -59,6 +59,12 @@ SMALL = [
     ((3, 5, 20), 128, "token", 0, 0),    # b=1: stage 2 alone
     ((4, 6, 10), 128, "custom", 0, 20),  # unaligned split
     ((1, 1, 1), 128, "dense", 0, 0),     # one token
+    # stage-2 groups of 33..128 rows (one workgroup of ceil(m / 32) waves per group)
+    ((81, 2, 3), 128, "frame", 0, 0),    # m=81 (the long layout's group size), three waves
+    ((40, 3, 2), 64, "frame", 0, 0),     # m=40, d=64, two waves
+    ((128, 1, 3), 128, "frame", 0, 0),   # m=128, four full waves
+    ((11, 3, 4), 128, "row", 0, 0),      # m=33: one row in the second wave
+    ((96, 2, 2), 128, "frame", 192, 0),  # tiled: m_tau=48 in two tiles
 ]
 
 
@@ -74,11 +80,11 @@ def test_backward_small_cases(grid, d, align, tile, cb):
         check(x, y, f"{grid} {align} t{tile} {name}")
 
 
-@pytest.mark.parametrize("name", ["frame_bf16", "row_bf16", "tiled_bf16"])
-def test_backward_full_size_two_heads(name):
+@pytest.mark.parametrize("name,heads", [("frame_bf16", 2), ("row_bf16", 2), ("tiled_bf16", 2), ("long_bf16", 1)])
+def test_backward_full_size(name, heads):
     c = datagen.CONFIGS[name]
-    q, k, v = datagen.config_inputs(name, heads=2)
-    g = datagen.qkv(1, 2, c["grid"], 128, (61, 62, 63), dtype=BF16)[0]
+    q, k, v = datagen.config_inputs(name, heads=heads)
+    g = datagen.qkv(1, heads, c["grid"], 128, (61, 62, 63), dtype=BF16)[0]
     got, plan, args = grads(q, k, v, g, c["grid"], c["align"], c["tile_tokens"])
     b = oracle.block_size(c["grid"], c["align"])
     want = oracle.monarch_backward(q, k, v, g, b, c["tile_tokens"])
@@ -91,7 +97,7 @@ def test_backward_full_size_two_heads(name):
         assert np.array_equal(x, to_np(y))
 
 
-SAVED = [SMALL[i] for i in (0, 1, 2, 5, 6, 8, 9)] + [((21, 30, 52), 128, "frame", 0, 0)]
+SAVED = [SMALL[i] for i in (0, 1, 2, 5, 6, 8, 9, 12)] + [((21, 30, 52), 128, "frame", 0, 0)]
 
 
 @pytest.mark.parametrize("grid,d,align,tile,cb", SAVED,
