@@ -73,8 +73,12 @@ hipError_t launch_bwd(const BwdArgs& b, hipStream_t stream);
 // dv, dv_delta; lse, delta, dq_in and dk_in are not used.
 bool bwd_small_supported(const GroupedArgs& g);
 hipError_t launch_bwd_small(const BwdArgs& b, hipStream_t stream);
-// The same for problems of 33..128 rows (the long layout's stage-2 groups): one
-// workgroup of ceil(L / 32) waves per problem; same arguments and outputs.
+// One-pass backward of a stage whose problems have at most 128 rows: one
+// workgroup of ceil(L / 32) waves per problem, lse and delta recomputed. Two
+// roles, picked by the output types: partial (dq, dk fp32; dv bf16; dv_delta;
+// as launch_bwd_small: the long layout's stage-2 groups) and final (dq, dk,
+// dv bf16, with the fp32 dq_in and dk_in added when given: the row layout's
+// stage-1 blocks). lse and delta are not used.
 bool bwd_group_supported(const GroupedArgs& g);
 hipError_t launch_bwd_group(const BwdArgs& b, hipStream_t stream);
 // out[r] = sum_c a[r][c] * b[r][c] over rows x D (bf16 or fp32 elements)

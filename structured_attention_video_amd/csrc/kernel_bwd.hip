@@ -441,6 +441,57 @@ __device__ __forceinline__ void stage_rows(char* t0, char* t1, const f32x16 (&x)
   __builtin_amdgcn_wave_barrier();
 }
 
+// As stage_rows for fp32 rows, but the stored rows are bf16 and, when
+// has_add, the fp32 rows of ra are added before the rounding (one rounding
+// of the sum): rows are staged in fp32, read back 16 bytes (4 channels) per
+// lane, the matching 16 bytes of ra loaded (consecutive lanes, consecutive
+// bytes), and 8 bytes per lane stored.
+template <int D>
+__device__ __forceinline__ void stage_rows_add(char* t0, char* t1, const f32x16 (&x)[D / 32], float mul,
+                                               __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t ra, bool has_add,
+                                               int64_t rs, int lane) {
+  constexpr int RB = D * 4, CH = D / 4, RPI = 64 / CH;
+  const int h = lane >> 5;
+  int r = lane & 31;
+  asm volatile("" : "+v"(r));
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier reads of the tiles are done
+  __builtin_amdgcn_wave_barrier();
+  char* t = r < 16 ? t0 : t1;
+  const int rr = r & 15;
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const u32x4 v = {__float_as_uint(x[mt][4 * g] * mul), __float_as_uint(x[mt][4 * g + 1] * mul),
+                       __float_as_uint(x[mt][4 * g + 2] * mul), __float_as_uint(x[mt][4 * g + 3] * mul)};
+      *reinterpret_cast<u32x4*>(t + rr * RB + 16 * ((8 * mt + 2 * g + h) ^ rr)) = v;
+    }
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  const uint32_t row_el = static_cast<uint32_t>(rs * D);
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int row = RPI * i + lane / CH, chk = lane % CH;
+    const char* tr = row < 16 ? t0 : t1;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tr + (row & 15) * RB + 16 * (chk ^ (row & 15)));
+    const uint32_t el = row * row_el + chk * 4;
+    float f[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
+    if (has_add) {
+      const u32x4 ad = bload16(ra, el * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f[e] += __uint_as_float(ad[e]);
+    }
+    bf16x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = static_cast<bf16>(f[e]);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), ro, static_cast<int>(el * 2), 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // the read-backs are done before the tiles are reused
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int D>
 __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
   constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * ROWB;
@@ -596,9 +647,13 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
 }
 
 // ---------------------------------------------------------------- mid-size problems, one pass
-// One workgroup of W = ceil(L / 32) waves per problem of 33..128 rows (the
-// long layout's stage-2 groups, m = 81), the multi-wave form of
-// bwd_small_kernel with the same inputs and outputs. Q, K, V (the stage's
+// One workgroup of W = ceil(L / 32) waves per problem of up to 128 rows (the
+// long layout's stage-2 groups, m = 81; the row layout's stage-1 blocks, b =
+// 52), the multi-wave form of bwd_small_kernel. Two roles: partial (FINAL
+// false, a stage-2 backward feeding stage 1: dQ, dK in fp32, dV in bf16 and
+// dv_delta, as bwd_small_kernel) and final (FINAL true, the last stage: dQ
+// and dK in bf16 with the fp32 dq_in and dk_in added before the rounding, dV
+// in bf16). In both, lse and delta are recomputed, not read. Q, K, V (the stage's
 // values) and G rows are copied whole into four swizzled 32W-row LDS tiles;
 // wave w owns rows 32w .. 32w+31.
 //   (a) lane = query: S^T and dP^T against every 32-key block, the row max,
@@ -613,7 +668,7 @@ __global__ void __launch_bounds__(64, 2) bwd_small_kernel(BwdArgs b) {
 // so each wave has a SIMD to itself and the register budget of a lone wave:
 // the three accumulators need not take turns. Outputs leave as whole rows
 // through the tiles once every wave is done with them.
-template <int D, int W>
+template <int D, int W, bool FINAL>
 __global__ void __launch_bounds__(64 * W, 1) bwd_group_kernel(BwdArgs b) {
   constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * W * ROWB;
   __shared__ __attribute__((aligned(1024))) char qt[TILE];
@@ -755,8 +810,10 @@ __global__ void __launch_bounds__(64 * W, 1) bwd_group_kernel(BwdArgs b) {
         }
       }
     }
-    const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, own + r, h));
-    if (h == 0 && own + r < L) b.dv_delta[hd * ntok + base + (own + r) * rs] = d1;
+    if constexpr (!FINAL) {
+      const float d1 = halves_sum(row_dot_acc<D>(dv, 1.f, true, vt, own + r, h));
+      if (h == 0 && own + r < L) b.dv_delta[hd * ntok + base + (own + r) * rs] = d1;
+    }
   }
   __syncthreads();  // every wave is done with every tile
 
@@ -765,10 +822,20 @@ __global__ void __launch_bounds__(64 * W, 1) bwd_group_kernel(BwdArgs b) {
   const int wl = L - own;  // >= 1: W = ceil(L / 32)
   const auto rdv = problem_rsrc(static_cast<const char*>(b.dv) + hoff * 2, wbase, rs, wl, D, 2);
   stage_rows<D, false>(qt + own * ROWB, qt + own * ROWB, dv, 1.f, rdv, rs, lane);
-  const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * 4, wbase, rs, wl, D, 4);
-  stage_rows<D, true>(kt + own * ROWB, vt + own * ROWB, dk, c * 0.6931471805599453f, rdk, rs, lane);
-  const auto rdq = problem_rsrc(static_cast<const char*>(b.dq) + hoff * 4, wbase, rs, wl, D, 4);
-  stage_rows<D, true>(gt + own * ROWB, qt + own * ROWB, dq, c * 0.6931471805599453f, rdq, rs, lane);
+  const float sc = c * 0.6931471805599453f;  // dQ, dK = scale * dS K, dS^T Q
+  if constexpr (FINAL) {
+    const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * 2, wbase, rs, wl, D, 2);
+    const auto rka = problem_rsrc(b.dk_in ? b.dk_in + hoff : b.dq, wbase, rs, wl, D, 4);
+    stage_rows_add<D>(kt + own * ROWB, vt + own * ROWB, dk, sc, rdk, rka, b.dk_in != nullptr, rs, lane);
+    const auto rdq = problem_rsrc(static_cast<const char*>(b.dq) + hoff * 2, wbase, rs, wl, D, 2);
+    const auto rqa = problem_rsrc(b.dq_in ? b.dq_in + hoff : b.dk, wbase, rs, wl, D, 4);
+    stage_rows_add<D>(gt + own * ROWB, qt + own * ROWB, dq, sc, rdq, rqa, b.dq_in != nullptr, rs, lane);
+  } else {
+    const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * 4, wbase, rs, wl, D, 4);
+    stage_rows<D, true>(kt + own * ROWB, vt + own * ROWB, dk, sc, rdk, rs, lane);
+    const auto rdq = problem_rsrc(static_cast<const char*>(b.dq) + hoff * 4, wbase, rs, wl, D, 4);
+    stage_rows<D, true>(gt + own * ROWB, qt + own * ROWB, dq, sc, rdq, rs, lane);
+  }
 }
 
 // 8 consecutive elements of a row as floats (one 16-byte load for bf16, two
@@ -858,25 +925,33 @@ hipError_t launch_bwd_small(const BwdArgs& b, hipStream_t s) {
 }
 
 bool bwd_group_supported(const GroupedArgs& g) {
-  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L > 32 && g.L <= 128 &&
+  return (g.D == 64 || g.D == 128) && g.qk_type == kBF16 && g.v_type == kBF16 && g.L >= 1 && g.L <= 128 &&
          g.q_row0 == 0 && g.Lq == g.L && (static_cast<int64_t>(128) + 32) * g.row_stride * g.D * 4 < (int64_t{1} << 31);
+}
+
+template <int D, bool FINAL>
+hipError_t launch_bwd_group_t(const BwdArgs& b, hipStream_t s) {
+  const GroupedArgs& g = b.g;
+  const int64_t nwg = static_cast<int64_t>(g.problems) * g.heads;
+  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const dim3 grid(static_cast<unsigned>(nwg));
+  switch ((g.L + 31) / 32) {
+    case 1: hipLaunchKernelGGL((bwd_group_kernel<D, 1, FINAL>), grid, dim3(64), 0, s, b); break;
+    case 2: hipLaunchKernelGGL((bwd_group_kernel<D, 2, FINAL>), grid, dim3(128), 0, s, b); break;
+    case 3: hipLaunchKernelGGL((bwd_group_kernel<D, 3, FINAL>), grid, dim3(192), 0, s, b); break;
+    default: hipLaunchKernelGGL((bwd_group_kernel<D, 4, FINAL>), grid, dim3(256), 0, s, b); break;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_group(const BwdArgs& b, hipStream_t s) {
   const GroupedArgs& g = b.g;
-  if (!bwd_group_supported(g) || !b.go || !b.dq || !b.dk || !b.dv || !b.dv_delta) return hipErrorInvalidValue;
-  const int64_t nwg = static_cast<int64_t>(g.problems) * g.heads;
-  if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  const dim3 grid(static_cast<unsigned>(nwg));
-  const int w = (g.L + 31) / 32;
-#define MONARCH_BWD_GROUP(DD, WW) hipLaunchKernelGGL((bwd_group_kernel<DD, WW>), grid, dim3(64 * WW), 0, s, b)
-  if (g.D == 128) {
-    if (w == 2) MONARCH_BWD_GROUP(128, 2); else if (w == 3) MONARCH_BWD_GROUP(128, 3); else MONARCH_BWD_GROUP(128, 4);
-  } else {
-    if (w == 2) MONARCH_BWD_GROUP(64, 2); else if (w == 3) MONARCH_BWD_GROUP(64, 3); else MONARCH_BWD_GROUP(64, 4);
-  }
-#undef MONARCH_BWD_GROUP
-  return hipGetLastError();
+  if (!bwd_group_supported(g) || !b.go || !b.dq || !b.dk || !b.dv || b.dv_type != kBF16) return hipErrorInvalidValue;
+  const bool final_role = b.dq_type == kBF16 && b.dk_type == kBF16;
+  const bool partial_role = b.dq_type == kF32 && b.dk_type == kF32 && b.dv_delta && !b.dq_in && !b.dk_in;
+  if (!final_role && !partial_role) return hipErrorInvalidValue;
+  if (g.D == 128) return final_role ? launch_bwd_group_t<128, true>(b, s) : launch_bwd_group_t<128, false>(b, s);
+  return final_role ? launch_bwd_group_t<64, true>(b, s) : launch_bwd_group_t<64, false>(b, s);
 }
 
 hipError_t launch_rowdot(const void* a, ElemType ta, const void* bp, ElemType tb, float* out, int64_t rows, int D,

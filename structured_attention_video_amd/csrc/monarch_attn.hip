@@ -436,16 +436,22 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
   // does the stage-2 forward recompute, its backward and stage 1's delta
   const GroupedArgs g2 = stage2_args(p, q, k, y, MONARCH_BF16, nullptr);
   const bool one32 = has1 && has2 && bwd_small_supported(g2);
-  const bool one128 = has1 && has2 && !one32 && bwd_group_supported(g2);
+  const bool one128 = has1 && has2 && !one32 && g2.L > 32 && bwd_group_supported(g2);
   const bool small2 = one32 || one128;
+  // the last stage's problems of at most 128 rows (the row layout's stage 1;
+  // stage 1 or stage 2 alone): one final-role launch recomputes its softmax
+  // and replaces the row-dot and the three tiled launches
+  const bool small1 = (has1 || !has2) && bwd_group_supported(stage1_args(p, q, k, v, y, MONARCH_BF16));
+  const bool solo2 = !has1 && has2 && bwd_group_supported(stage2_args(p, q, k, v, MONARCH_BF16, nullptr));
 
   // forward again, keeping Y and the per-row statistics (or, from a training
-  // forward's saved state, only the argument set-up)
+  // forward's saved state, only the argument set-up); a lone stage 1 done in
+  // one pass needs neither
   GroupedArgs f1{}, f2{};
   if (has1 || !has2) {
     f1 = stage1_args(p, q, k, v, y, MONARCH_BF16);
     f1.lse = lse1;
-    if (!saved && !ok(launch(choose_kernel(f1, p.flags), f1, s))) return MONARCH_ERR_HIP;
+    if (!saved && (has2 || !small1) && !ok(launch(choose_kernel(f1, p.flags), f1, s))) return MONARCH_ERR_HIP;
   }
   if (small2) {
     BwdArgs b2{};
@@ -457,7 +463,16 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
     b2.dv_delta = del1;
     if (!ok(one32 ? launch_bwd_small(b2, s) : launch_bwd_group(b2, s))) return MONARCH_ERR_HIP;
   }
-  if (has2 && !small2) {
+  if (solo2) {
+    BwdArgs b2{};
+    b2.g = stage2_args(p, q, k, v, MONARCH_BF16, nullptr);
+    b2.go = grad_o;
+    b2.dq = grad_q; b2.dq_type = kBF16;
+    b2.dk = grad_k; b2.dk_type = kBF16;
+    b2.dv = grad_v; b2.dv_type = kBF16;
+    if (!ok(launch_bwd_group(b2, s))) return MONARCH_ERR_HIP;
+  }
+  if (has2 && !small2 && !solo2) {
     // values: Y (or V when stage 1 is the identity). The recomputed output is
     // kept in fp32 (in the dQ2 section, free until the stage-2 backward): delta
     // = rowsum(G * O) then uses O before its bf16 rounding, which matters
@@ -467,7 +482,7 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
     f2.lse = lse2;
     if (!ok(launch(choose_kernel(f2, p.flags), f2, s))) return MONARCH_ERR_HIP;
   }
-  if (has2 && !small2) {
+  if (has2 && !small2 && !solo2) {
     BwdArgs b2{};
     b2.g = f2;
     b2.go = grad_o;
@@ -491,7 +506,8 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
     b1.go = has2 ? dy : grad_o;
     b1.lse = lse1;
     b1.delta = del1;
-    if (!small2 && !ok(launch_rowdot(b1.go, kBF16, has2 ? y : o, kBF16, del1, rows, D, s))) return MONARCH_ERR_HIP;
+    if (!small2 && !small1 && !ok(launch_rowdot(b1.go, kBF16, has2 ? y : o, kBF16, del1, rows, D, s)))
+      return MONARCH_ERR_HIP;
     b1.dq = grad_q; b1.dq_type = kBF16;
     b1.dk = grad_k; b1.dk_type = kBF16;
     b1.dv = grad_v; b1.dv_type = kBF16;
@@ -499,7 +515,7 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
       b1.dq_in = dq2;
       b1.dk_in = dk2;
     }
-    if (!ok(launch_bwd(b1, s))) return MONARCH_ERR_HIP;
+    if (!ok(small1 ? launch_bwd_group(b1, s) : launch_bwd(b1, s))) return MONARCH_ERR_HIP;
   }
   return MONARCH_OK;
 }
