@@ -225,7 +225,6 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   const auto rg = problem_rsrc(static_cast<const bf16*>(b.go) + hoff, base, rs, L, D, 2);
   const bool kf32 = b.dk_type == kF32, vf32 = b.dv_type == kF32;
   const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * (kf32 ? 4 : 2), base, rs, L, D, kf32 ? 4 : 2);
-  const auto rdv = problem_rsrc(static_cast<const char*>(b.dv) + hoff * (vf32 ? 4 : 2), base, rs, L, D, vf32 ? 4 : 2);
   const auto ra = problem_rsrc(b.dk_in ? b.dk_in + hoff : b.delta, base, rs, L, D, 4);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
@@ -333,8 +332,23 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   if (j < n) step(j, q0, g0, q1, g1, 0);
 
   const int r = key0 + (lane & 31);
-  if (MODE == 1) store_rows<D>(rdk, kf32, ra, b.dk_in != nullptr, r, rs, acc, c * 0.6931471805599453f, lane);
-  else store_rows<D>(rdv, vf32, ra, false, r, rs, acc, 1.f, lane);
+  if constexpr (MODE == 1) {
+    store_rows<D>(rdk, kf32, ra, b.dk_in != nullptr, r, rs, acc, c * 0.6931471805599453f, lane);
+  } else if (key0 < L) {
+    // dV rows leave whole, staged through this wave's own (dead) Q or G slot:
+    // measured 2.4% (frame) and 6.5% (row layout, rows 52 tokens apart)
+    // faster than 8-byte pieces of 32 rows; for the dK and dQ kernels the
+    // same change measured slower at the frame shape
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    char* t = wv == 0 ? q0 : wv == 1 ? q1 : wv == 2 ? g0 : g1;
+    const int64_t wb = base + key0 * rs;
+    const auto rw = problem_rsrc(static_cast<const char*>(b.dv) + hoff * (vf32 ? 4 : 2), wb, rs, L - key0, D,
+                                 vf32 ? 4 : 2);
+    if (vf32)
+      stage_rows<D, true>(t, t + 64 * D, acc, 1.f, rw, rs, lane);
+    else
+      stage_rows<D, false>(t, t, acc, 1.f, rw, rs, lane);
+  }
 }
 
 // ---------------------------------------------------------------- small problems, one pass
@@ -377,119 +391,6 @@ __device__ __forceinline__ float row_dot_acc(const f32x16 (&x)[D / 32], float mu
       }
     }
   return acc;
-}
-
-// One wave stores its 32 rows of x^T accumulators (lane: row lane % 32,
-// channels 32 mt + 8 (i / 4) + 4 h + i % 4), scaled by mul, as whole rows
-// through LDS: written into the wave's dead tiles, read back 16 bytes per lane
-// (fp32 rows: two or four per instruction; bf16 rows: four or eight), stored
-// with one instruction per 1 KB. fp32 rows go to t0 (rows 0..15) and t1
-// (rows 16..31), 16-byte chunk c of row r at c ^ (r % 16); bf16 rows to t0
-// in the tile swizzle. Rows past the problem's end are dropped by ro.
-template <int D, bool F32>
-__device__ __forceinline__ void stage_rows(char* t0, char* t1, const f32x16 (&x)[D / 32], float mul,
-                                           __amdgpu_buffer_rsrc_t ro, int64_t rs, int lane) {
-  const int h = lane >> 5;
-  int r = lane & 31;
-  asm volatile("" : "+v"(r));
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier reads of the tiles are done
-  __builtin_amdgcn_wave_barrier();
-  if constexpr (F32) {
-    constexpr int RB = D * 4, CH = D / 4, RPI = 64 / CH;
-    char* t = r < 16 ? t0 : t1;
-    const int rr = r & 15;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x4 v = {__float_as_uint(x[mt][4 * g] * mul), __float_as_uint(x[mt][4 * g + 1] * mul),
-                         __float_as_uint(x[mt][4 * g + 2] * mul), __float_as_uint(x[mt][4 * g + 3] * mul)};
-        *reinterpret_cast<u32x4*>(t + rr * RB + 16 * ((8 * mt + 2 * g + h) ^ rr)) = v;
-      }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    const uint32_t row_bytes = static_cast<uint32_t>(rs * D * 4);
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int row = RPI * i + lane / CH, chk = lane % CH;
-      const char* tr = row < 16 ? t0 : t1;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(tr + (row & 15) * RB + 16 * (chk ^ (row & 15)));
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(row * row_bytes + chk * 16), 0, 0);
-    }
-  } else {
-    constexpr int CPR = D / 8, RPI = 64 / CPR;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(x[mt][4 * g + e] * mul);
-        *reinterpret_cast<bf16x4*>(t0 + swoff<D>(r, 4 * mt + g) + 8 * h) = v;
-      }
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
-    const uint32_t row_bytes = static_cast<uint32_t>(rs * D * 2);
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int row = RPI * i + lane / CPR, chk = lane % CPR;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(t0 + swoff<D>(row, chk));
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>(row * row_bytes + chk * 16), 0, 0);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // the read-backs are done before the tiles are reused
-  __builtin_amdgcn_wave_barrier();
-}
-
-// As stage_rows for fp32 rows, but the stored rows are bf16 and, when
-// has_add, the fp32 rows of ra are added before the rounding (one rounding
-// of the sum): rows are staged in fp32, read back 16 bytes (4 channels) per
-// lane, the matching 16 bytes of ra loaded (consecutive lanes, consecutive
-// bytes), and 8 bytes per lane stored.
-template <int D>
-__device__ __forceinline__ void stage_rows_add(char* t0, char* t1, const f32x16 (&x)[D / 32], float mul,
-                                               __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t ra, bool has_add,
-                                               int64_t rs, int lane) {
-  constexpr int RB = D * 4, CH = D / 4, RPI = 64 / CH;
-  const int h = lane >> 5;
-  int r = lane & 31;
-  asm volatile("" : "+v"(r));
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): earlier reads of the tiles are done
-  __builtin_amdgcn_wave_barrier();
-  char* t = r < 16 ? t0 : t1;
-  const int rr = r & 15;
-#pragma unroll
-  for (int mt = 0; mt < D / 32; ++mt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const u32x4 v = {__float_as_uint(x[mt][4 * g] * mul), __float_as_uint(x[mt][4 * g + 1] * mul),
-                       __float_as_uint(x[mt][4 * g + 2] * mul), __float_as_uint(x[mt][4 * g + 3] * mul)};
-      *reinterpret_cast<u32x4*>(t + rr * RB + 16 * ((8 * mt + 2 * g + h) ^ rr)) = v;
-    }
-  __builtin_amdgcn_s_waitcnt(0xc07f);
-  __builtin_amdgcn_wave_barrier();
-  const uint32_t row_el = static_cast<uint32_t>(rs * D);
-#pragma unroll
-  for (int i = 0; i < 32 / RPI; ++i) {
-    const int row = RPI * i + lane / CH, chk = lane % CH;
-    const char* tr = row < 16 ? t0 : t1;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(tr + (row & 15) * RB + 16 * (chk ^ (row & 15)));
-    const uint32_t el = row * row_el + chk * 4;
-    float f[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) f[e] = __uint_as_float(v[e]);
-    if (has_add) {
-      const u32x4 ad = bload16(ra, el * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) f[e] += __uint_as_float(ad[e]);
-    }
-    bf16x4 w;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = static_cast<bf16>(f[e]);
-    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, w), ro, static_cast<int>(el * 2), 0, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // the read-backs are done before the tiles are reused
-  __builtin_amdgcn_wave_barrier();
 }
 
 template <int D>

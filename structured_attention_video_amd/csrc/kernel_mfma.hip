@@ -287,7 +287,14 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   if (a.lse && h == 0 && row0 + r < Lq)
     a.lse[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = st.m + __builtin_amdgcn_logf(lsum);
   if constexpr (OUT_F32) {
-    store_out<D, true, POLICY>(ro, row0 + r, rs, st.o, 1.f / lsum, lane);
+    // fp32 rows (4 D bytes each) staged 16 at a time through this wave's
+    // half of a K slot, then stored whole
+    char* stage = (wave < 2 ? k0 : k1) + (wave & 1) * 32 * (D * 2);
+    const uint32_t row_bytes = static_cast<uint32_t>(rs * D * 4);  // offsets fit 32 bits (offsets_fit)
+    if constexpr (POLICY == 0)
+      stage_rows_f32_halves<D>(stage, st.o, 1.f / lsum, ro, rs, lane, static_cast<uint32_t>(row0) * row_bytes);
+    else
+      store_out<D, true, POLICY>(ro, row0 + r, rs, st.o, 1.f / lsum, lane);
   } else {
     // Stage this wave's 32 rows in its own half of a K slot (no wave reads K
     // after the loop), swizzled, then store whole rows (16-byte pieces of
