@@ -131,6 +131,11 @@ struct TileDma {
       src_off[i] = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
     }
   }
+  // copy instruction i of this wave's share alone
+  __device__ __forceinline__ void dma1(char* tile, __amdgpu_buffer_rsrc_t src, uint32_t tile_off, int wave,
+                                       int i) const {
+    lds_dma16(src, tile + (RW * wave + T::RPI * i) * T::ROWB, src_off[i] + tile_off);
+  }
   __device__ __forceinline__ void dma(char* tile, __amdgpu_buffer_rsrc_t src, uint32_t tile_off, int wave) const {
 #pragma unroll
     for (int i = 0; i < IPW; ++i) lds_dma16(src, tile + (RW * wave + T::RPI * i) * T::ROWB, src_off[i] + tile_off);

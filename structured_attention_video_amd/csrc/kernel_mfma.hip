@@ -79,11 +79,12 @@ __device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const F
 // Scores of the next tile interleaved with the probabilities of the current
 // one: each 16-channel step (two MFMAs, K read one step ahead) carries a
 // slice of the exponentials; sched_barrier keeps the steps apart so the
-// compiler does not regroup all MFMAs first.
-template <int D>
+// compiler does not regroup all MFMAs first. hook(ks) runs after step ks's
+// MFMAs are issued (the caller's tile copies go there).
+template <int D, typename Hook>
 __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* kl, const FlashOffsets<D>& fo,
                                                   const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
-                                                  bf16x8 (&pb)[4], float& l, float c, float m) {
+                                                  bf16x8 (&pb)[4], float& l, float c, float m, Hook&& hook) {
   constexpr int KS = D / 16;
   constexpr int PER = 32 / KS;  // weights per step, even
   sn[0] = f32x16{};
@@ -99,6 +100,7 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
     }
     sn[0] = mma(a0, qf[ks], sn[0]);
     sn[1] = mma(a1, qf[ks], sn[1]);
+    hook(ks);
 #pragma unroll
     for (int e = 0; e < PER; e += 2) {
       const int i = ks * PER + e;
@@ -238,15 +240,26 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   // the copies first.
   auto step = [&](int j, char* kdma, char* vdma, const char* kread, const char* vread, const f32x16 (&s)[2],
                   f32x16 (&sn)[2]) {
-    if (j + 2 < n) td.dma(kdma, rk, (j + 2) * tile_bytes, wave);
-    td.dma(vdma, rv, (j + 1) * tile_bytes, wave);
+    // copies of V_{j+1} and K_{j+2}: waves without rows issue them here,
+    // the others between their score steps (below)
+    const bool kc = j + 2 < n;
+    if (!active) td.dma(vdma, rv, (j + 1) * tile_bytes, wave);
+    if (!active && kc) td.dma(kdma, rk, (j + 2) * tile_bytes, wave);
     if (active) {
       update_max<D>(s, st.o, st.m, st.l, c);
       bf16x8 pb[4];
 #if MONARCH_PRIO == 2
       __builtin_amdgcn_s_setprio(1);
 #endif
-      scores_with_probs<D>(sn, kread, fo, qf, s, pb, st.l, c, st.m);
+      // the wave's copy instructions go one per score step (V's first, then
+      // K's) instead of back to back before them: stage 1 at the frame shape
+      // measured 1.7% faster
+      scores_with_probs<D>(sn, kread, fo, qf, s, pb, st.l, c, st.m, [&](int ks) {
+        constexpr int IPW = TileDma<D, NW>::IPW;
+        static_assert(2 * IPW <= D / 16, "one copy instruction per score step");
+        if (ks < IPW) td.dma1(vdma, rv, (j + 1) * tile_bytes, wave, ks);
+        if (ks >= IPW && ks < 2 * IPW && kc) td.dma1(kdma, rk, (j + 2) * tile_bytes, wave, ks - IPW);
+      });
 #if MONARCH_PRIO == 1
       __builtin_amdgcn_s_setprio(1);
 #endif
