@@ -739,6 +739,188 @@ __global__ void __launch_bounds__(64 * W, 1) bwd_group_kernel(BwdArgs b) {
   }
 }
 
+// Final-role form for problems of at most 64 rows (the row layout's stage-1
+// blocks, b = 52) with half the LDS: two 32W-row tiles instead of four, and
+// 256 registers, so that four workgroups (two waves per SIMD) share a CU.
+// Phase (a) (lane = query) runs with K and V in the tiles and this wave's Q
+// and G rows loaded straight into registers; dQ (bf16, plus dq_in) leaves
+// through the tiles once every wave has read its own K and V rows into
+// registers; Q and G are then copied into the same tiles (this wave's rows
+// come back from L2) for phase (b) (lane = key), where lse and delta enter as
+// a bias K-step (as bwd_dkdv MODE 1) and dV and dK take one sweep each (S is
+// computed twice: the accumulators do not fit together). Measured at the row
+// layout: 321 us against 433 us for bwd_group_kernel.
+template <int D, int W>
+__global__ void __launch_bounds__(64 * W, 2) bwd_group2_kernel(BwdArgs b) {
+  constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB, IPW = 32 / RPI, TILE = 32 * W * ROWB;
+  __shared__ __attribute__((aligned(1024))) char ta[TILE];
+  __shared__ __attribute__((aligned(1024))) char tb[TILE];
+  __shared__ __attribute__((aligned(16))) float xl[32 * W];
+  __shared__ __attribute__((aligned(16))) float xd[32 * W];
+  const GroupedArgs& a = b.g;
+  const int p = blockIdx.x % a.problems, hd = blockIdx.x / a.problems;
+  const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
+  const int64_t base = problem_base(a, p);
+  const int64_t rs = a.row_stride;
+  const int L = a.L;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, r = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int own = 32 * wave;
+  const float c = a.scale_log2;
+  const auto rq = problem_rsrc(static_cast<const bf16*>(a.q) + hoff, base, rs, L, D, 2);
+  const auto rk = problem_rsrc(static_cast<const bf16*>(a.k) + hoff, base, rs, L, D, 2);
+  const auto rv = problem_rsrc(static_cast<const bf16*>(a.v) + hoff, base, rs, L, D, 2);
+  const auto rg = problem_rsrc(static_cast<const bf16*>(b.go) + hoff, base, rs, L, D, 2);
+  auto copy = [&](char* t, __amdgpu_buffer_rsrc_t src) {  // this wave's 32 rows of a tile
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int row = own + RPI * i + lane / CPR;
+      const int ch = (lane % CPR) ^ swz<D>(row);
+      lds_dma16(src, t + (own + RPI * i) * ROWB, static_cast<uint32_t>((row * rs * D + ch * 8) * 2));
+    }
+  };
+  copy(ta, rk);
+  copy(tb, rv);
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    bf16x8 qf[D / 16], gf[D / 16];
+    load_qfrag<D>(qf, rq, own, rs, lane);
+    load_qfrag<D>(gf, rg, own, rs, lane);
+    wait_dma();
+    __syncthreads();
+    const FlashOffsets<D> fo(0, lane, rs);
+
+    // (a) lane = query own + r
+    f32x16 s[W], dp[W];
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        s[kb] = mma(k_operand<D>(ta, fo, ks, kb), qf[ks], s[kb]);
+        dp[kb] = mma(k_operand<D>(tb, fo, ks, kb), gf[ks], dp[kb]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (32 * kb + acc_key(i, h) >= L) s[kb][i] = -INFINITY;
+        mx = fmaxf(mx, s[kb][i]);
+      }
+    mx = halves_max(mx) * c;
+    float l = 0.f, pd = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        s[kb][i] = fast_exp2(fmaf(s[kb][i], c, -mx));
+        l += s[kb][i];
+        pd = fmaf(s[kb][i], dp[kb][i], pd);
+      }
+    l = halves_sum(l);
+    const float inv = 1.f / l;
+    const float del = halves_sum(pd) * inv;
+    if (h == 0) {
+      xl[own + r] = mx + __builtin_amdgcn_logf(l);
+      xd[own + r] = del;
+    }
+    f32x16 dq[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+#pragma unroll
+    for (int kb = 0; kb < W; ++kb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dp[kb][i] = s[kb][i] * inv * (dp[kb][i] - del);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 ds = p_operand(dp[kb], st);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mma(v_operand<D>(ta, fo, mt, 2 * kb + st), ds, dq[mt]);
+      }
+    }
+    // this wave's K and V rows for (b), then the tiles are free
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = ld_bf16x8(ta + swoff<D>(own + r, 2 * ks + h));
+      vf[ks] = ld_bf16x8(tb + swoff<D>(own + r, 2 * ks + h));
+    }
+    __syncthreads();
+    const int64_t wbase = base + own * rs;
+    const int wl = L - own;  // >= 1: W = ceil(L / 32)
+    const auto rdq = problem_rsrc(static_cast<const char*>(b.dq) + hoff * 2, wbase, rs, wl, D, 2);
+    const auto rqa = problem_rsrc(b.dq_in ? b.dq_in + hoff : b.dk, wbase, rs, wl, D, 4);
+    stage_rows_add<D>(ta + own * ROWB, tb + own * ROWB, dq, c * 0.6931471805599453f, rdq, rqa,
+                      b.dq_in != nullptr, rs, lane);
+  }
+  __syncthreads();  // every wave's staging reads are done: refill the tiles
+  copy(ta, rq);
+  copy(tb, rg);
+  wait_dma();
+  __syncthreads();
+
+  // (b) lane = key own + r, in two sweeps over the query blocks (S again in
+  // the second): dV (stored directly, the tiles are still in use), then dK;
+  // S - lse/c and dP - delta come straight from the accumulators (bias K-step:
+  // lane r of the A operand carries query 32qb + r)
+  const int64_t wbase = base + own * rs;
+  const int wl = L - own;
+  const FlashOffsets<D> fo(0, lane, rs);
+  const bf16x8 ones = bias_ones(h);
+  const float inv_c = 1.f / c;
+  {
+    f32x16 dv[D / 32];
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) dv[mt] = f32x16{};
+#pragma unroll
+    for (int qb = 0; qb < W; ++qb) {
+      f32x16 s = {};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) s = mma(k_operand<D>(ta, fo, ks, qb), kf[ks], s);
+      s = mma(bias_operand(-xl[32 * qb + r] * inv_c, h), ones, s);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] = fast_exp2(s[i] * c);  // P
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const bf16x8 pp = p_operand(s, st);
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dv[mt] = mma(v_operand<D>(tb, fo, mt, 2 * qb + st), pp, dv[mt]);
+      }
+    }
+    const auto rdv = problem_rsrc(static_cast<const char*>(b.dv) + hoff * 2, wbase, rs, wl, D, 2);
+    store_rows<D>(rdv, false, rdv, false, r, rs, dv, 1.f, lane);
+  }
+  f32x16 dk[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dk[mt] = f32x16{};
+#pragma unroll
+  for (int qb = 0; qb < W; ++qb) {
+    f32x16 s = {}, dp = {};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      s = mma(k_operand<D>(ta, fo, ks, qb), kf[ks], s);
+      dp = mma(k_operand<D>(tb, fo, ks, qb), vf[ks], dp);
+    }
+    s = mma(bias_operand(-xl[32 * qb + r] * inv_c, h), ones, s);
+    dp = mma(bias_operand(-xd[32 * qb + r], h), ones, dp);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) dp[i] *= fast_exp2(s[i] * c);  // dS = P (dP - delta)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const bf16x8 ps = p_operand(dp, st);
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) dk[mt] = mma(v_operand<D>(ta, fo, mt, 2 * qb + st), ps, dk[mt]);
+    }
+  }
+  __syncthreads();  // every wave is done with both tiles
+  const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * 2, wbase, rs, wl, D, 2);
+  const auto rka = problem_rsrc(b.dk_in ? b.dk_in + hoff : b.dq, wbase, rs, wl, D, 4);
+  stage_rows_add<D>(ta + own * ROWB, tb + own * ROWB, dk, c * 0.6931471805599453f, rdk, rka, b.dk_in != nullptr,
+                    rs, lane);
+}
+
 // 8 consecutive elements of a row as floats (one 16-byte load for bf16, two
 // for fp32)
 template <bool F32>
@@ -836,6 +1018,13 @@ hipError_t launch_bwd_group_t(const BwdArgs& b, hipStream_t s) {
   const int64_t nwg = static_cast<int64_t>(g.problems) * g.heads;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
   const dim3 grid(static_cast<unsigned>(nwg));
+  if constexpr (FINAL) {
+    if (g.L <= 64) {
+      if (g.L <= 32) hipLaunchKernelGGL((bwd_group2_kernel<D, 1>), grid, dim3(64), 0, s, b);
+      else hipLaunchKernelGGL((bwd_group2_kernel<D, 2>), grid, dim3(128), 0, s, b);
+      return hipGetLastError();
+    }
+  }
   switch ((g.L + 31) / 32) {
     case 1: hipLaunchKernelGGL((bwd_group_kernel<D, 1, FINAL>), grid, dim3(64), 0, s, b); break;
     case 2: hipLaunchKernelGGL((bwd_group_kernel<D, 2, FINAL>), grid, dim3(128), 0, s, b); break;
