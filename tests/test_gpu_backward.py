@@ -65,6 +65,9 @@ SMALL = [
     ((128, 1, 3), 128, "frame", 0, 0),   # m=128, four full waves
     ((11, 3, 4), 128, "row", 0, 0),      # m=33: one row in the second wave
     ((96, 2, 2), 128, "frame", 192, 0),  # tiled: m_tau=48 in two tiles
+    ((40, 4, 33), 128, "frame", 0, 0),   # b=132 (tiled stage-1 kernels, which read the one-pass
+                                         # stage 2's delta), m=40
+    ((72, 2, 66), 64, "frame", 0, 0),    # the same with m=72 (three waves), d=64
     # a lone stage of at most 128 rows, done in one pass (final gradients)
     ((2, 4, 12), 128, "dense", 0, 0),    # stage 1 alone, N=96
     ((2, 5, 10), 64, "token", 0, 0),     # stage 2 alone, N=100
