@@ -40,6 +40,9 @@ struct GroupedArgs {
   float* lse;         // optional (bf16 MFMA and tiny kernels): per query row, log2 of the
                       // softmax denominator in the exp2 domain, i.e. the row's probabilities
                       // are exp2(scale_log2 * <q,k> - lse); indexed [head][token]
+  const void* dg;     // optional, flash kernel only, with delta: bf16 rows G (layout of q);
+  float* delta;       // then, instead of O, delta[row] = sum over channels of G * O with O in
+                      // fp32 before any rounding, indexed [head][token] (o is not written)
 };
 
 // Backward of one grouped-attention stage (the chain rule of O = P V with

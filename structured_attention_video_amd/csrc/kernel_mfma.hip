@@ -186,7 +186,7 @@ struct FlashState {
 // the barriers. Every copy it issues has completed when it returns; waves
 // whose rows lie outside the tile or past the end of the problem only copy,
 // and return early (after the last barrier).
-template <int D, bool OUT_F32, int POLICY = 0, int NW = 4>
+template <int D, bool OUT_F32, int POLICY = 0, int NW = 4, bool DELTA = false>
 __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, int qt, int qrows, char* k0,
                                            char* k1, char* v0, char* v1, int tid) {
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
@@ -299,7 +299,29 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   asm volatile("" : "+v"(r));
   if (a.lse && h == 0 && row0 + r < Lq)
     a.lse[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = st.m + __builtin_amdgcn_logf(lsum);
-  if constexpr (OUT_F32) {
+  if constexpr (DELTA) {
+    // delta of this lane's query row instead of O: the sum over channels of G
+    // times O (fp32, before any rounding); register i of tile mt holds channel
+    // 32 mt + 8 (i / 4) + 4 h + i % 4, read from G 4 channels (8 bytes) at a time
+    const auto rg = problem_rsrc(static_cast<const bf16*>(a.dg) + hoff, qbase, rs, Lq, D, 2);
+    const uint32_t rowel = static_cast<uint32_t>(row0 + r) * static_cast<uint32_t>(rs * D);
+    const float inv = 1.f / lsum;
+    float acc = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 gv = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg, static_cast<int>((rowel + 32 * mt + 8 * g + 4 * h) * 2), 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t bits = (e & 1) ? (gv[e >> 1] & 0xffff0000u) : (gv[e >> 1] << 16);
+          acc = fmaf(st.o[mt][4 * g + e] * inv, __uint_as_float(bits), acc);
+        }
+      }
+    const float d = halves_sum(acc);
+    if (h == 0 && row0 + r < Lq) a.delta[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = d;
+  } else if constexpr (OUT_F32) {
     // fp32 rows (4 D bytes each) staged 16 at a time through this wave's
     // half of a K slot, then stored whole
     char* stage = (wave < 2 ? k0 : k1) + (wave & 1) * 32 * (D * 2);
@@ -348,7 +370,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
 // every barrier, so their MFMA and softmax phases stop overlapping.
 constexpr int kFlashWaves = 4;
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool DELTA = false>
 __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs a, int qtiles, int qrows, int nwg) {
   using T = SwTile<D>;
   __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
@@ -358,8 +380,8 @@ __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs 
   const int id = xcd_order(blockIdx.x, nwg);
   const int qt = id % qtiles;
   const int rest = id / qtiles;
-  flash_tile<D, OUT_F32, 0, kFlashWaves>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1, v0, v1,
-                                         threadIdx.x);
+  flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1, v0,
+                                                v1, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- group
@@ -665,7 +687,7 @@ bool offsets_fit(const GroupedArgs& a, int pad_rows) {
   return (static_cast<int64_t>(a.L) + pad_rows) * a.row_stride * a.D * 4 < (int64_t{1} << 31);
 }
 
-template <int D, bool F32>
+template <int D, bool F32, bool DELTA = false>
 hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   // query rows in units of one wave's 32, spread evenly over the fewest
   // tiles of at most kFlashWaves units (a 1560-row block: 49 units, 13 tiles
@@ -676,7 +698,7 @@ hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   const int qrows = 32 * ((units + qtiles - 1) / qtiles);
   const int64_t nwg = static_cast<int64_t>(qtiles) * a.problems * a.heads;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((flash_kernel<D, F32>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0, s, a,
+  hipLaunchKernelGGL((flash_kernel<D, F32, DELTA>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0, s, a,
                      qtiles, qrows, static_cast<int>(nwg));
   return hipGetLastError();
 }
@@ -707,6 +729,10 @@ bool flash_supported(const GroupedArgs& a) { return mfma_types_ok(a) && a.L > 12
 
 hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
   if (!flash_supported(a)) return hipErrorInvalidValue;
+  if (a.delta) {  // row sums of G * O instead of O
+    if (!a.dg) return hipErrorInvalidValue;
+    return a.D == 128 ? launch_flash_t<128, true, true>(a, s) : launch_flash_t<64, true, true>(a, s);
+  }
   const bool f32 = a.o_type == kF32;
   if (a.D == 128) return f32 ? launch_flash_t<128, true>(a, s) : launch_flash_t<128, false>(a, s);
   return f32 ? launch_flash_t<64, true>(a, s) : launch_flash_t<64, false>(a, s);

@@ -472,15 +472,26 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
     b2.dv = grad_v; b2.dv_type = kBF16;
     if (!ok(launch_bwd_group(b2, s))) return MONARCH_ERR_HIP;
   }
+  bool delta2_done = false;
   if (has2 && !small2 && !solo2) {
-    // values: Y (or V when stage 1 is the identity). The recomputed output is
-    // kept in fp32 (in the dQ2 section, free until the stage-2 backward): delta
-    // = rowsum(G * O) then uses O before its bf16 rounding, which matters
-    // because dS = P * (dP - delta) subtracts two nearly equal numbers.
+    // values: Y (or V when stage 1 is the identity). delta = rowsum(G * O)
+    // uses O before its bf16 rounding, which matters because dS = P * (dP -
+    // delta) subtracts two nearly equal numbers: the flash kernel forms it in
+    // its epilogue from the fp32 O in registers; otherwise the recomputed
+    // output is kept in fp32 (in the dQ2 section, free until the stage-2
+    // backward) for a row-dot launch.
     f2 = stage2_args(p, q, k, has1 ? y : v, MONARCH_BF16, dq2);
     f2.o_type = kF32;
     f2.lse = lse2;
-    if (!ok(launch(choose_kernel(f2, p.flags), f2, s))) return MONARCH_ERR_HIP;
+    const int32_t k2 = choose_kernel(f2, p.flags);
+    if (k2 == kKernelFlash) {
+      f2.dg = grad_o;
+      f2.delta = del2;
+      delta2_done = true;
+    }
+    if (!ok(launch(k2, f2, s))) return MONARCH_ERR_HIP;
+    f2.dg = nullptr;
+    f2.delta = nullptr;
   }
   if (has2 && !small2 && !solo2) {
     BwdArgs b2{};
@@ -488,7 +499,7 @@ monarch_status backward_impl(const monarch_plan* plan, const void* q, const void
     b2.go = grad_o;
     b2.lse = lse2;
     b2.delta = del2;
-    if (!ok(launch_rowdot(grad_o, kBF16, dq2, kF32, del2, rows, D, s))) return MONARCH_ERR_HIP;
+    if (!delta2_done && !ok(launch_rowdot(grad_o, kBF16, dq2, kF32, del2, rows, D, s))) return MONARCH_ERR_HIP;
     if (has1) {  // partial dQ, dK in fp32; dY (bf16) feeds stage 1
       b2.dq = dq2; b2.dq_type = kF32;
       b2.dk = dk2; b2.dk_type = kF32;
