@@ -178,9 +178,11 @@ size_t monarch_attn_backward_workspace_size(const monarch_plan* plan);
  * and grad_o = dL/dO, writes grad_q = dL/dQ, grad_k = dL/dK, grad_v = dL/dV. All nine arrays are
  * [batch, heads, N, head_dim] bf16 device arrays (bf16 plans only; fp32 plans return
  * MONARCH_ERR_UNSUPPORTED); o must be the output of monarch_attn_forward for the same inputs.
- * Stage 1 is recomputed (Y and per-row softmax statistics of both stages go to the workspace,
- * whose contents on entry are ignored), then the stage-2 backward and the stage-1 backward run,
- * fp32 accumulation throughout; Q and K receive the sum of both stages' gradients. grad_* must
+ * Stage 1 is recomputed (its output Y and per-row softmax statistics go to the workspace, whose
+ * contents on entry are ignored; a plan whose only stage has at most 128 rows per problem skips
+ * it), then the stage-2 backward and the stage-1 backward run, fp32 accumulation throughout;
+ * stages with at most 128 rows per problem recompute their softmax statistics inside their
+ * one-pass backward. Q and K receive the sum of both stages' gradients. grad_* must
  * not overlap each other, the inputs or the workspace. Asynchronous on `stream`. */
 monarch_status monarch_attn_backward(const monarch_plan* plan, const void* q, const void* k, const void* v,
                                      const void* o, const void* grad_o, void* grad_q, void* grad_k,
