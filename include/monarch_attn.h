@@ -25,9 +25,10 @@
  *
  * Ownership: the caller owns every device buffer. A plan holds host metadata
  * only; it never allocates device memory. No entry point allocates device
- * memory, synchronises the host, or keeps global mutable state, so forwards on
- * different streams with different workspaces may run concurrently with one
- * plan.
+ * memory or synchronises the host, and apart from monarch_attn_forward_noalloc
+ * (which works in a static device array of the library) none keeps global
+ * mutable state, so forwards on different streams with different workspaces may
+ * run concurrently with one plan.
  *
  * Errors: every argument, plan and pointer check returns its status before any
  * HIP call, so these paths are testable on a machine without a GPU. A failed
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 3
+#define MONARCH_ABI_VERSION 4
 
 typedef enum monarch_status {
   MONARCH_OK = 0,
@@ -54,7 +55,9 @@ typedef enum monarch_status {
                                    or a device pointer not 16-byte aligned */
   MONARCH_ERR_WORKSPACE = 4,    /* workspace null or smaller than monarch_attn_workspace_size() */
   MONARCH_ERR_ALIAS = 5,        /* output overlaps an input or the workspace */
-  MONARCH_ERR_HIP = 6           /* a HIP launch failed */
+  MONARCH_ERR_HIP = 6,          /* a HIP launch failed */
+  MONARCH_ERR_TOO_LARGE = 7     /* monarch_attn_forward_noalloc: the plan's workspace exceeds the
+                                   library's static scratch (MONARCH_NOALLOC_SCRATCH_BYTES) */
 } monarch_status;
 
 typedef enum monarch_dtype {
@@ -139,6 +142,22 @@ monarch_status monarch_attn_plan_info(const monarch_plan* plan, monarch_plan_inf
 monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, const void* k,
                                     const void* v, void* o, void* workspace,
                                     size_t workspace_bytes, void* stream);
+
+/* The forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): monarch_attn_forward with the
+ * workspace taken from a static device array inside the library instead of a caller argument.
+ * Arguments, checks, launches and output as monarch_attn_forward; the call makes no device
+ * allocation or free. The array holds MONARCH_NOALLOC_SCRATCH_BYTES bytes on every GPU the
+ * library runs on, from the time the library's code is loaded there until the process ends; a
+ * plan whose workspace (monarch_attn_workspace_size) is larger returns MONARCH_ERR_TOO_LARGE
+ * before any HIP call. The array of the current device is used; `stream`, when not NULL, must
+ * belong to the current device (else MONARCH_ERR_INVALID_ARG). All calls on one GPU share that
+ * GPU's array and it keeps the last call's contents: calls that overlap in time on one GPU (on
+ * different streams, or from different threads without ordering) race and give undefined
+ * results. Asynchronous on `stream`. */
+#define MONARCH_NOALLOC_SCRATCH_BYTES (128ll << 20)
+monarch_status monarch_attn_forward_noalloc(const monarch_plan* plan, const void* q, const void* k,
+                                            const void* v, void* o, void* stream);
 
 /* Stage 1 alone (the right factor, contiguous blocks): writes Y, an array of the plan's y_dtype
  * and shape [batch, heads, N, head_dim], of y_bytes >= workspace size. When m_tau = 1 Y is the

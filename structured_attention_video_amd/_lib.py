@@ -15,12 +15,15 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MONARCH_ATTN_LIB") or os.path.join(_HERE, "libmonarch_attn.so")
 
 # status codes (monarch_status)
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_UNALIGNED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP = range(7)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_UNALIGNED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOO_LARGE = range(8)
 STATUS_NAMES = {
     OK: "MONARCH_OK", ERR_INVALID_ARG: "MONARCH_ERR_INVALID_ARG",
     ERR_UNSUPPORTED: "MONARCH_ERR_UNSUPPORTED", ERR_UNALIGNED: "MONARCH_ERR_UNALIGNED",
     ERR_WORKSPACE: "MONARCH_ERR_WORKSPACE", ERR_ALIAS: "MONARCH_ERR_ALIAS", ERR_HIP: "MONARCH_ERR_HIP",
+    ERR_TOO_LARGE: "MONARCH_ERR_TOO_LARGE",
 }
+# bytes of the static device array monarch_attn_forward_noalloc works in (MONARCH_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 128 << 20
 # monarch_dtype
 BF16, FP32 = 0, 1
 # monarch_align
@@ -34,6 +37,7 @@ EXPORTED = [
     "monarch_attn_stage2", "monarch_status_string", "monarch_attn_kernel_name",
     "monarch_attn_abi_version", "monarch_attn_backward_workspace_size", "monarch_attn_backward",
     "monarch_attn_chunk_forward", "monarch_attn_forward_train", "monarch_attn_backward_saved",
+    "monarch_attn_forward_noalloc",
 ]
 
 
@@ -98,5 +102,7 @@ def lib() -> ctypes.CDLL:
     L.monarch_attn_forward_train.restype = i32
     L.monarch_attn_backward_saved.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.monarch_attn_backward_saved.restype = i32
+    L.monarch_attn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.monarch_attn_forward_noalloc.restype = i32
     _lib = L
     return L

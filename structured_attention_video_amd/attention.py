@@ -128,6 +128,18 @@ class MonarchPlan:
         _check(st, "monarch_attn_forward")
         return out
 
+    def forward_noalloc(self, q, k, v, out):
+        """forward() with the workspace taken from the library's static device array
+        (monarch_attn_forward_noalloc): the library allocates nothing; `out` is required."""
+        self._check_io(q, k, v, out)
+        for t in (q, k, v, out):
+            if t.dtype != self.dtype:
+                raise ValueError(f"dtype {t.dtype} != plan dtype {self.dtype}")
+        st = _lib.lib().monarch_attn_forward_noalloc(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                     out.data_ptr(), self._stream(q))
+        _check(st, "monarch_attn_forward_noalloc")
+        return out
+
     def stage1(self, q, k, v, y=None):
         self._check_io(q, k, v)
         ydt = self.y_dtype if self.info["m_tau"] > 1 else self.dtype

@@ -5,6 +5,7 @@
 
 #include <math.h>
 #include <string.h>
+#include <mutex>
 #include <new>
 
 #include "internal.h"
@@ -148,6 +149,41 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + static_cast<uintptr_t>(nb) && y < x + static_cast<uintptr_t>(na);
 }
 
+// ---------------------------------------------------------------- static scratch
+// Device memory of monarch_attn_forward_noalloc: the forward's workspace (Y, and a fused plan's
+// control block) for callers that cannot allocate. Each GPU the library runs on holds its own
+// copy of this array from the time the code object is loaded there until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: its device address is
+// taken once per device with hipGetSymbolAddress (with that device current) and only that
+// address is ever passed on.
+constexpr int64_t kScratchBytes = MONARCH_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of the current device's scratch array (the stream, when given, must belong to
+// the current device).
+monarch_status scratch_address(void* stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MONARCH_ERR_HIP;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) return MONARCH_ERR_HIP;
+    if (sdev != dev) return MONARCH_ERR_INVALID_ARG;
+  }
+  if (dev < 0 || dev >= kMaxScratchDevices) return MONARCH_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MONARCH_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MONARCH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -251,24 +287,20 @@ static monarch_status run_stage2(const monarch_plan_info& p, const void* q, cons
   return launch(p.stage2_kernel, a, s) == hipSuccess ? MONARCH_OK : MONARCH_ERR_HIP;
 }
 
-monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, const void* k,
-                                    const void* v, void* o, void* workspace, size_t workspace_bytes,
-                                    void* stream) {
+// Argument checks of the forward that need no workspace (plain host arithmetic).
+static monarch_status forward_io_checks(const monarch_plan* plan, const void* q, const void* k, const void* v,
+                                        const void* o) {
   if (!plan || !q || !k || !v || !o) return MONARCH_ERR_INVALID_ARG;
   const monarch_plan_info& p = plan->info;
   if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(o)) return MONARCH_ERR_UNALIGNED;
   const int64_t io = tensor_bytes(p, p.dtype);
-  const int64_t ws = p.workspace_bytes;
-  if (ws > 0) {
-    if (!workspace || static_cast<int64_t>(workspace_bytes) < ws) return MONARCH_ERR_WORKSPACE;
-    if (misaligned(workspace)) return MONARCH_ERR_UNALIGNED;
-  }
   if (overlap(o, io, q, io) || overlap(o, io, k, io) || overlap(o, io, v, io)) return MONARCH_ERR_ALIAS;
-  if (ws > 0 && (overlap(o, io, workspace, ws) || overlap(workspace, ws, q, io) ||
-                 overlap(workspace, ws, k, io) || overlap(workspace, ws, v, io)))
-    return MONARCH_ERR_ALIAS;
+  return MONARCH_OK;
+}
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
+// The forward's launches, once every argument has been checked.
+static monarch_status forward_launch(const monarch_plan_info& p, const void* q, const void* k, const void* v,
+                                     void* o, void* workspace, hipStream_t s) {
   const bool has1 = p.b > 1, has2 = p.m_tau > 1;
   if (!has2) return run_stage1(p, q, k, v, o, p.dtype, s);  // second factor is the identity
   if (!has1) return run_stage2(p, q, k, v, p.dtype, o, s);  // first factor is the identity: Y = V
@@ -285,6 +317,38 @@ monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, con
   monarch_status st = run_stage1(p, q, k, v, workspace, p.y_dtype, s);
   if (st != MONARCH_OK) return st;
   return run_stage2(p, q, k, workspace, p.y_dtype, o, s);
+}
+
+monarch_status monarch_attn_forward(const monarch_plan* plan, const void* q, const void* k,
+                                    const void* v, void* o, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+  const monarch_status chk = forward_io_checks(plan, q, k, v, o);
+  if (chk != MONARCH_OK) return chk;
+  const monarch_plan_info& p = plan->info;
+  const int64_t io = tensor_bytes(p, p.dtype);
+  const int64_t ws = p.workspace_bytes;
+  if (ws > 0) {
+    if (!workspace || static_cast<int64_t>(workspace_bytes) < ws) return MONARCH_ERR_WORKSPACE;
+    if (misaligned(workspace)) return MONARCH_ERR_UNALIGNED;
+    if (overlap(o, io, workspace, ws) || overlap(workspace, ws, q, io) || overlap(workspace, ws, k, io) ||
+        overlap(workspace, ws, v, io))
+      return MONARCH_ERR_ALIAS;
+  }
+  return forward_launch(p, q, k, v, o, workspace, static_cast<hipStream_t>(stream));
+}
+
+monarch_status monarch_attn_forward_noalloc(const monarch_plan* plan, const void* q, const void* k,
+                                            const void* v, void* o, void* stream) {
+  const monarch_status chk = forward_io_checks(plan, q, k, v, o);
+  if (chk != MONARCH_OK) return chk;
+  const monarch_plan_info& p = plan->info;
+  if (p.workspace_bytes > kScratchBytes) return MONARCH_ERR_TOO_LARGE;
+  void* ws = nullptr;
+  if (p.workspace_bytes > 0) {
+    const monarch_status st = scratch_address(stream, &ws);
+    if (st != MONARCH_OK) return st;
+  }
+  return forward_launch(p, q, k, v, o, ws, static_cast<hipStream_t>(stream));
 }
 
 monarch_status monarch_attn_stage1(const monarch_plan* plan, const void* q, const void* k,
@@ -554,6 +618,7 @@ const char* monarch_status_string(monarch_status status) {
     case MONARCH_ERR_WORKSPACE: return "workspace missing or too small";
     case MONARCH_ERR_ALIAS: return "output overlaps an input or the workspace";
     case MONARCH_ERR_HIP: return "HIP launch failed";
+    case MONARCH_ERR_TOO_LARGE: return "workspace exceeds the library's static scratch (no-allocation forward)";
   }
   return "unknown status";
 }

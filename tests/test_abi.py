@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.monarch_attn_abi_version() == 3
+    assert L.monarch_attn_abi_version() == 4
 
 
 def _plan(batch=1, heads=2, d=128, grid=(4, 6, 10), align=0, custom_b=0, tile=0, dtype=0,
@@ -152,6 +152,24 @@ def test_forward_errors(plan):
     assert _fwd(plan, ws=A + STEP) == _lib.ERR_ALIAS                 # workspace overlaps k
 
 
+def test_noalloc_forward_errors(plan):
+    """Argument errors of the no-allocation forward return before any HIP call."""
+    fwd = L.monarch_attn_forward_noalloc
+    assert fwd(None, A, A + STEP, A + 2 * STEP, A + 3 * STEP, None) == _lib.ERR_INVALID_ARG
+    assert fwd(plan, A, A + STEP, A + 2 * STEP, None, None) == _lib.ERR_INVALID_ARG
+    assert fwd(plan, A, A + STEP + 8, A + 2 * STEP, A + 3 * STEP, None) == _lib.ERR_UNALIGNED
+    assert fwd(plan, A, A + STEP, A + 2 * STEP, A + 16, None) == _lib.ERR_ALIAS
+    # 12 heads of the 81x30x52 grid: 388 MB of Y, more than the static scratch
+    st, big = _plan(heads=12, grid=(81, 30, 52))
+    assert st == _lib.OK and L.monarch_attn_workspace_size(big) > _lib.NOALLOC_SCRATCH_BYTES
+    assert fwd(big, A, A + (1 << 32), A + (2 << 32), A + (3 << 32), None) == _lib.ERR_TOO_LARGE
+    L.monarch_attn_destroy(big)
+    # 12 heads of the 21x30x52 grid fit (100.6 MB)
+    st, frame = _plan(heads=12, grid=(21, 30, 52))
+    assert L.monarch_attn_workspace_size(frame) <= _lib.NOALLOC_SCRATCH_BYTES
+    L.monarch_attn_destroy(frame)
+
+
 def test_stage_entry_errors(plan):
     io = 2 * 240 * 128 * 2
     assert L.monarch_attn_stage1(plan, A, A + STEP, A + 2 * STEP, None, io, None) == _lib.ERR_INVALID_ARG
@@ -168,7 +186,7 @@ def test_stage_entry_errors(plan):
 
 
 def test_status_strings_and_kernel_names():
-    for code in range(7):
+    for code in range(8):
         assert L.monarch_status_string(code)
     assert L.monarch_status_string(99) == b"unknown status"
     for kid in range(6):
