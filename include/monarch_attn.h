@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 4
+#define MONARCH_ABI_VERSION 5
 
 typedef enum monarch_status {
   MONARCH_OK = 0,
@@ -79,13 +79,28 @@ typedef enum monarch_align {
 #define MONARCH_FLAG_Y_FP32 (1u << 0)          /* keep Y in fp32 for bf16 inputs (default: bf16) */
 #define MONARCH_FLAG_ALLOW_UNALIGNED (1u << 1) /* accept a custom b that cuts a grid axis */
 #define MONARCH_FLAG_GENERIC (1u << 2)         /* force the plain VALU kernels (diagnostics) */
-/* One launch for both stages (the fused variant the explainer's kernel section describes, run
- * as a persistent launch): stage-2 groups start as soon as the stage-1 blocks of their head and
- * tile are done, filling the end of stage 1 instead of waiting for all of it. Used only where it
- * applies (bf16, Y bf16, b > 128, 2 <= m_tau <= 32: the frame and tiled alignments); elsewhere
- * the flag is ignored and monarch_plan_info.fused reports 0. It adds a small control block to
- * the workspace. */
+/* One launch for both stages, run as a persistent launch (a design choice of this library; the
+ * pages describe no fused two-stage kernel): stage-2 groups start as soon as the stage-1 blocks
+ * of their head and tile are done, filling the end of stage 1 instead of waiting for all of it.
+ * Used only where it applies (bf16, Y bf16, b > 128, 2 <= m_tau <= 32: the frame and tiled
+ * alignments); elsewhere the flag is ignored and monarch_plan_info.fused reports 0. It adds a
+ * small control block to the workspace. */
 #define MONARCH_FLAG_FUSED (1u << 3)
+/* One refinement step of the Monarch factors. The pages say MonarchAttention fits its factors by
+ * iterative refinement (about ten steps) and that MonarchRT needs a single step after finetuning
+ * (explainer section 2.C; Spanish explainer, Resumen Ejecutivo section 2, Metodologia B); they
+ * print no update equations. Reading fixed by this library: softmax attention maximises
+ * F(A) = sum_r <A_r, S_r> + H(A_r) (S = s Q K^T, H the entropy) over row-stochastic A; a step
+ * maximises F over the Monarch matrices one factor at a time, starting from an identity stage-2
+ * factor. One step keeps stage 1 as in the direct forward (Y = R V) and refits stage 2:
+ *   Kbar[u,i,j] = sum_j' R_{u,i}[j,j'] K[u,i,j']   (stage 1 applied to the keys),
+ *   h[u,i,j]    = entropy (bits) of row j of R_{u,i},
+ *   O[u,i,j]    = sum_i' softmax_i'(s <Q[u,i,j], Kbar[u,i',j]> + h[u,i',j] ln 2) Y[u,i',j].
+ * With b = 1 or m_tau = 1 it equals the direct forward. Kbar is kept in the input dtype. The
+ * workspace then holds Y, Kbar and h (monarch_attn_workspace_size). monarch_attn_forward and
+ * monarch_attn_forward_noalloc compute it; monarch_attn_stage1 is unchanged (Y); stage2, chunk,
+ * backward and training calls return MONARCH_ERR_UNSUPPORTED. Overrides MONARCH_FLAG_FUSED. */
+#define MONARCH_FLAG_REFINE (1u << 4)
 
 typedef struct monarch_plan monarch_plan;
 
@@ -106,6 +121,10 @@ typedef struct monarch_plan_info {
   int32_t stage1_kernel; /* variant id, see monarch_attn_kernel_name() */
   int32_t stage2_kernel;
   int32_t fused;         /* 1: monarch_attn_forward makes one fused launch (MONARCH_FLAG_FUSED) */
+  int32_t refine_steps;  /* 1: the forward applies one refinement step (MONARCH_FLAG_REFINE), else 0 */
+  int64_t fused_error_offset; /* fused plans: byte offset in the workspace of the int32 error word
+                                 (nonzero after a forward whose stage-2 wait timed out; that
+                                 forward's O then holds NaN rows); -1 for other plans */
 } monarch_plan_info;
 
 /* Validate a problem and build a plan (host only, no HIP call).

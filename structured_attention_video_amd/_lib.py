@@ -10,9 +10,8 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-# MONARCH_ATTN_LIB may point at another build of the same library (e.g. a
-# tuning variant); by default the in-tree build is loaded.
-LIB_PATH = os.environ.get("MONARCH_ATTN_LIB") or os.path.join(_HERE, "libmonarch_attn.so")
+# always the in-tree build (structured_attention_video_amd/build.py writes it)
+LIB_PATH = os.path.join(_HERE, "libmonarch_attn.so")
 
 # status codes (monarch_status)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_UNALIGNED, ERR_WORKSPACE, ERR_ALIAS, ERR_HIP, ERR_TOO_LARGE = range(8)
@@ -29,7 +28,7 @@ BF16, FP32 = 0, 1
 # monarch_align
 ALIGN = {"frame": 0, "row": 1, "dense": 2, "token": 3, "custom": 4}
 # flags
-FLAG_Y_FP32, FLAG_ALLOW_UNALIGNED, FLAG_GENERIC, FLAG_FUSED = 1, 2, 4, 8
+FLAG_Y_FP32, FLAG_ALLOW_UNALIGNED, FLAG_GENERIC, FLAG_FUSED, FLAG_REFINE = 1, 2, 4, 8, 16
 
 EXPORTED = [
     "monarch_attn_plan", "monarch_attn_destroy", "monarch_attn_workspace_size",
@@ -50,6 +49,7 @@ class PlanInfo(ctypes.Structure):
         ("scale", ctypes.c_float), ("flags", ctypes.c_uint32), ("workspace_bytes", ctypes.c_int64),
         ("flops_stage1", ctypes.c_int64), ("flops_stage2", ctypes.c_int64),
         ("stage1_kernel", ctypes.c_int32), ("stage2_kernel", ctypes.c_int32), ("fused", ctypes.c_int32),
+        ("refine_steps", ctypes.c_int32), ("fused_error_offset", ctypes.c_int64),
     ]
 
     def as_dict(self):

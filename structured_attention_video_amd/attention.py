@@ -35,13 +35,15 @@ class MonarchPlan:
 
     align: "frame" (b = H*W), "row" (b = W), "dense" (b = N), "token" (b = 1)
     or "custom" (b = custom_b). tile_tokens: 0/None = untiled. dtype: torch
-    dtype or "bf16"/"fp32".
+    dtype or "bf16"/"fp32". refine: one refinement step of the factors
+    (MONARCH_FLAG_REFINE).
     """
 
     def __init__(self, batch: int, heads: int, head_dim: int, grid: Sequence[int],
                  align: str = "frame", custom_b: int = 0, tile_tokens: Optional[int] = None,
                  dtype=torch.bfloat16, scale: Optional[float] = None, y_fp32: bool = False,
-                 allow_unaligned: bool = False, generic: bool = False, fused: bool = False):
+                 allow_unaligned: bool = False, generic: bool = False, fused: bool = False,
+                 refine: bool = False):
         L = _lib.lib()
         if isinstance(dtype, str):
             dtype = _DTYPE_NAMES[dtype]
@@ -49,7 +51,8 @@ class MonarchPlan:
             raise ValueError(f"unsupported dtype {dtype}")
         self.dtype = dtype
         flags = ((_lib.FLAG_Y_FP32 if y_fp32 else 0) | (_lib.FLAG_ALLOW_UNALIGNED if allow_unaligned else 0)
-                 | (_lib.FLAG_GENERIC if generic else 0) | (_lib.FLAG_FUSED if fused else 0))
+                 | (_lib.FLAG_GENERIC if generic else 0) | (_lib.FLAG_FUSED if fused else 0)
+                 | (_lib.FLAG_REFINE if refine else 0))
         T, H, W = (int(x) for x in grid)
         handle = ctypes.c_void_p()
         st = L.monarch_attn_plan(ctypes.byref(handle), batch, heads, head_dim, T, H, W,
@@ -85,9 +88,7 @@ class MonarchPlan:
         Reads device memory (synchronises); for tests and diagnostics."""
         if not self.fused:
             return 0
-        ybytes = self.shape[0] * self.shape[1] * self.shape[2] * self.shape[3] * (
-            4 if self.y_dtype == torch.float32 else 2)
-        off = (ybytes + 255) // 256 * 256 + 8 * 4
+        off = int(self.info["fused_error_offset"])
         return int(workspace[off:off + 4].view(torch.int32).item())
 
     @property
@@ -95,12 +96,22 @@ class MonarchPlan:
         return self.info["flops_stage1"] + self.info["flops_stage2"]
 
     # -- helpers
-    def _check_io(self, *ts):
+    def _check_io(self, *ts, dtype=None):
+        """GPU, contiguous, the plan's shape and (default) the plan's element type: the
+        C ABI takes bare pointers, so these checks are what bounds its reads and writes."""
+        want = self.dtype if dtype is None else dtype
         for t in ts:
             if not isinstance(t, torch.Tensor) or not t.is_cuda:
                 raise ValueError("tensors must be GPU tensors")
             if tuple(t.shape) != self.shape or not t.is_contiguous():
                 raise ValueError(f"expected contiguous {self.shape}, got {tuple(t.shape)}")
+            if t.dtype != want:
+                raise ValueError(f"dtype {t.dtype} != expected {want}")
+
+    @staticmethod
+    def _check_workspace(ws):
+        if not isinstance(ws, torch.Tensor) or not ws.is_cuda or not ws.is_contiguous():
+            raise ValueError("the workspace must be a contiguous GPU tensor")
 
     @staticmethod
     def _stream(t: torch.Tensor):
@@ -113,14 +124,13 @@ class MonarchPlan:
     # -- entry points
     def forward(self, q, k, v, out=None, workspace=None):
         self._check_io(q, k, v)
-        for t in (q, k, v):
-            if t.dtype != self.dtype:
-                raise ValueError(f"dtype {t.dtype} != plan dtype {self.dtype}")
         if out is None:
             out = torch.empty_like(q)
         self._check_io(out)
         if workspace is None:
             workspace = self.new_workspace(q.device)
+        if workspace is not None:
+            self._check_workspace(workspace)
         ws_ptr = workspace.data_ptr() if workspace is not None else None
         ws_n = workspace.numel() * workspace.element_size() if workspace is not None else 0
         st = _lib.lib().monarch_attn_forward(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(),
@@ -132,9 +142,6 @@ class MonarchPlan:
         """forward() with the workspace taken from the library's static device array
         (monarch_attn_forward_noalloc): the library allocates nothing; `out` is required."""
         self._check_io(q, k, v, out)
-        for t in (q, k, v, out):
-            if t.dtype != self.dtype:
-                raise ValueError(f"dtype {t.dtype} != plan dtype {self.dtype}")
         st = _lib.lib().monarch_attn_forward_noalloc(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                                      out.data_ptr(), self._stream(q))
         _check(st, "monarch_attn_forward_noalloc")
@@ -145,15 +152,19 @@ class MonarchPlan:
         ydt = self.y_dtype if self.info["m_tau"] > 1 else self.dtype
         if y is None:
             y = torch.empty(self.shape, dtype=ydt, device=q.device)
+        self._check_io(y, dtype=ydt)
         st = _lib.lib().monarch_attn_stage1(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                             y.data_ptr(), y.numel() * y.element_size(), self._stream(q))
         _check(st, "monarch_attn_stage1")
         return y
 
     def stage2(self, q, k, y, out=None):
-        self._check_io(q, k, y)
+        self._check_io(q, k)
+        # Y has the plan's Y type, or the input type when stage 1 is the identity (b = 1: Y is V)
+        self._check_io(y, dtype=self.y_dtype if self.info["b"] > 1 else self.dtype)
         if out is None:
             out = torch.empty_like(q)
+        self._check_io(out)
         st = _lib.lib().monarch_attn_stage2(self._h, q.data_ptr(), k.data_ptr(), y.data_ptr(),
                                             out.data_ptr(), self._stream(q))
         _check(st, "monarch_attn_stage2")
@@ -166,8 +177,7 @@ class MonarchPlan:
         and y (the stage-1 cache) of frames < t0; writes y and out of the chunk."""
         self._check_io(q, k, v, out)
         if y is not None:
-            if tuple(y.shape) != self.shape or not y.is_contiguous() or y.dtype != self.y_dtype or not y.is_cuda:
-                raise ValueError("y must be a contiguous GPU tensor of the plan's shape and Y dtype")
+            self._check_io(y, dtype=self.y_dtype)
         st = _lib.lib().monarch_attn_chunk_forward(self._h, int(t0), int(t1), q.data_ptr(), k.data_ptr(),
                                                    v.data_ptr(), y.data_ptr() if y is not None else None,
                                                    out.data_ptr(), self._stream(q))
@@ -189,6 +199,7 @@ class MonarchPlan:
         n = self.backward_workspace_bytes
         if workspace is None:
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        self._check_workspace(workspace)
         ws_n = workspace.numel() * workspace.element_size()
         st = _lib.lib().monarch_attn_forward_train(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                                    out.data_ptr(), workspace.data_ptr(), ws_n, self._stream(q))
@@ -203,15 +214,13 @@ class MonarchPlan:
         if saved and workspace is None:
             raise ValueError("saved=True needs the workspace forward_train returned")
         self._check_io(q, k, v, o, grad_o)
-        for t in (q, k, v, o, grad_o):
-            if t.dtype != self.dtype:
-                raise ValueError(f"dtype {t.dtype} != plan dtype {self.dtype}")
         if grads is None:
             grads = tuple(torch.empty_like(q) for _ in range(3))
         self._check_io(*grads)
         n = self.backward_workspace_bytes
         if workspace is None:
             workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=q.device)
+        self._check_workspace(workspace)
         ws_n = workspace.numel() * workspace.element_size()
         fn = _lib.lib().monarch_attn_backward_saved if saved else _lib.lib().monarch_attn_backward
         st = fn(self._h, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), grad_o.data_ptr(),

@@ -43,6 +43,11 @@ struct GroupedArgs {
   const void* dg;     // optional, flash kernel only, with delta: bf16 rows G (layout of q);
   float* delta;       // then, instead of O, delta[row] = sum over channels of G * O with O in
                       // fp32 before any rounding, indexed [head][token] (o is not written)
+  float* ent;         // optional (flash, group and generic kernels): per query row, the
+                      // Shannon entropy in bits of the row's softmax weights, [head][token]
+  const float* kbias; // optional (group, tiny and generic kernels): per key row, a bias in
+                      // bits added to the row's logits, i.e. weights ~ exp2(scale_log2 * <q,k>
+                      // + kbias[key]); indexed [head][token]
 };
 
 // Backward of one grouped-attention stage (the chain rule of O = P V with
@@ -112,6 +117,7 @@ struct FusedArgs {
 };
 bool fused_supported(const GroupedArgs& s1, const GroupedArgs& s2);
 int64_t fused_ctl_ints(int64_t heads, int64_t tiles);
+int64_t fused_ctl_error_index();  // int index of the error word in the control block
 hipError_t launch_fused(const FusedArgs& f, hipStream_t stream);
 
 // Each launcher returns hipSuccess or the launch error.

@@ -61,7 +61,9 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
     qr[e] = row_ok ? load_elem(a.q, qrow + part * PART + e, a.qk_type) * a.scale_log2 : 0.f;
     acc[e] = 0.f;
   }
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f, wsum = 0.f;
+  const int64_t rows_off = static_cast<int64_t>(h) * (a.head_elems / D);
+  const float* kb = a.kbias ? a.kbias + rows_off + base : nullptr;
 
   for (int k0 = 0; k0 < a.L; k0 += KC) {
     const int nk = min(KC, a.L - k0);
@@ -87,18 +89,23 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
 #pragma unroll
       for (int e = 0; e < PART; ++e) s = fmaf(qr[e], ks[part][j][e], s);
       if (SPLIT == 2) s += __shfl_xor(s, 1);
+      if (kb && j < nk) s += kb[static_cast<int64_t>(k0 + j) * a.row_stride];
       sc[j] = (j < nk) ? s : -INFINITY;
       cmax = fmaxf(cmax, sc[j]);
     }
     const float m_new = fmaxf(m, cmax);
     const float alpha = exp2f(m - m_new);
+    // wsum: sum of p * (logit - running max) in bits, moved to the new maximum
+    wsum = l > 0.f ? alpha * fmaf(m - m_new, l, wsum) : 0.f;
     l *= alpha;
 #pragma unroll
     for (int e = 0; e < PART; ++e) acc[e] *= alpha;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
-      const float pj = exp2f(sc[j] - m_new);
+      const float z = sc[j] - m_new;
+      const float pj = exp2f(z);
       l += pj;
+      if (pj > 0.f) wsum = fmaf(pj, z, wsum);
 #pragma unroll
       for (int e = 0; e < PART; ++e) acc[e] = fmaf(pj, vs[part][j][e], acc[e]);
     }
@@ -109,6 +116,8 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
     const float inv = 1.f / l;
 #pragma unroll
     for (int e = 0; e < PART; ++e) store_elem(a.o, qrow + part * PART + e, acc[e] * inv, a.o_type);
+    if (a.ent && part == 0)
+      a.ent[rows_off + base + static_cast<int64_t>(row) * a.row_stride] = log2f(l) - wsum * inv;
   }
 }
 

@@ -32,8 +32,9 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(
 
 // Running max update with lazy rescale of the accumulator. The tile maximum
 // is a max3 tree over the lane's 32 scores (16 instructions).
-template <int D>
-__device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m, float& l, float c) {
+template <int D, bool ENT = false>
+__device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m, float& l, float& w,
+                                           float c) {
   float t[12];
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
@@ -48,6 +49,8 @@ __device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D /
   if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold)) {
     const float mn = fmaxf(m, mx);
     const float alpha = fast_exp2(m - mn);
+    // w (entropy rows only): the sum of p (logit - max), moved to the new maximum
+    if constexpr (ENT) w = l > 0.f ? alpha * fmaf(m - mn, l, w) : 0.f;
     l *= alpha;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
@@ -81,10 +84,11 @@ __device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const F
 // slice of the exponentials; sched_barrier keeps the steps apart so the
 // compiler does not regroup all MFMAs first. hook(ks) runs after step ks's
 // MFMAs are issued (the caller's tile copies go there).
-template <int D, typename Hook>
+template <int D, bool ENT, typename Hook>
 __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* kl, const FlashOffsets<D>& fo,
                                                   const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
-                                                  bf16x8 (&pb)[4], float& l, float c, float m, Hook&& hook) {
+                                                  bf16x8 (&pb)[4], float& l, float& w, float c, float m,
+                                                  Hook&& hook) {
   constexpr int KS = D / 16;
   constexpr int PER = 32 / KS;  // weights per step, even
   sn[0] = f32x16{};
@@ -104,10 +108,15 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
 #pragma unroll
     for (int e = 0; e < PER; e += 2) {
       const int i = ks * PER + e;
-      const float p0 = fast_exp2(fmaf(s[i >> 4][i & 15], c, -m));
-      const float p1 = fast_exp2(fmaf(s[(i + 1) >> 4][(i + 1) & 15], c, -m));
+      const float z0 = fmaf(s[i >> 4][i & 15], c, -m), z1 = fmaf(s[(i + 1) >> 4][(i + 1) & 15], c, -m);
+      const float p0 = fast_exp2(z0);
+      const float p1 = fast_exp2(z1);
       pp[i >> 1] = bf16x2{static_cast<bf16>(p0), static_cast<bf16>(p1)};
       l = sum2(pp[i >> 1], l);
+      if constexpr (ENT) {
+        if (p0 > 0.f) w = fmaf(p0, z0, w);
+        if (p1 > 0.f) w = fmaf(p1, z1, w);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     a0 = n0;
@@ -121,16 +130,24 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
 }
 
 // exp2(s*c - m) as bf16 B operands for the four 16-key PV steps (last tile)
-__device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float c, float m) {
+template <bool ENT>
+__device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float& w, float c,
+                                      float m) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     bf16x2 pp[4];
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-      const float p0 = fast_exp2(fmaf(s[st >> 1][8 * (st & 1) + e], c, -m));
-      const float p1 = fast_exp2(fmaf(s[st >> 1][8 * (st & 1) + e + 1], c, -m));
+      const float z0 = fmaf(s[st >> 1][8 * (st & 1) + e], c, -m);
+      const float z1 = fmaf(s[st >> 1][8 * (st & 1) + e + 1], c, -m);
+      const float p0 = fast_exp2(z0);
+      const float p1 = fast_exp2(z1);
       pp[e >> 1] = bf16x2{static_cast<bf16>(p0), static_cast<bf16>(p1)};
       l = sum2(pp[e >> 1], l);
+      if constexpr (ENT) {
+        if (p0 > 0.f) w = fmaf(p0, z0, w);
+        if (p1 > 0.f) w = fmaf(p1, z1, w);
+      }
     }
     pb[st] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -175,6 +192,7 @@ template <int D>
 struct FlashState {
   f32x16 o[D / 32];  // O^T accumulators
   float m, l;        // running max (scaled) and partial sum
+  float w;           // entropy rows only: partial sum of p (logit - max)
 };
 
 // Query tile qt (rows qt*qrows .. +qrows, qrows a multiple of 32 and at most
@@ -186,7 +204,7 @@ struct FlashState {
 // the barriers. Every copy it issues has completed when it returns; waves
 // whose rows lie outside the tile or past the end of the problem only copy,
 // and return early (after the last barrier).
-template <int D, bool OUT_F32, int POLICY = 0, int NW = 4, bool DELTA = false>
+template <int D, bool OUT_F32, int POLICY = 0, int NW = 4, bool DELTA = false, bool ENT = false>
 __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, int qt, int qrows, char* k0,
                                            char* k1, char* v0, char* v1, int tid) {
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
@@ -224,6 +242,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   for (int mt = 0; mt < D / 32; ++mt) st.o[mt] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
+  st.w = 0.f;
   wait_dma();
   __syncthreads();
 
@@ -246,7 +265,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
     if (!active) td.dma(vdma, rv, (j + 1) * tile_bytes, wave);
     if (!active && kc) td.dma(kdma, rk, (j + 2) * tile_bytes, wave);
     if (active) {
-      update_max<D>(s, st.o, st.m, st.l, c);
+      update_max<D, ENT>(s, st.o, st.m, st.l, st.w, c);
       bf16x8 pb[4];
 #if MONARCH_PRIO == 2
       __builtin_amdgcn_s_setprio(1);
@@ -254,7 +273,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
       // the wave's copy instructions go one per score step (V's first, then
       // K's) instead of back to back before them: stage 1 at the frame shape
       // measured 1.7% faster
-      scores_with_probs<D>(sn, kread, fo, qf, s, pb, st.l, c, st.m, [&](int ks) {
+      scores_with_probs<D, ENT>(sn, kread, fo, qf, s, pb, st.l, st.w, c, st.m, [&](int ks) {
         constexpr int IPW = TileDma<D, NW>::IPW;
         static_assert(2 * IPW <= D / 16, "one copy instruction per score step");
         if (ks < IPW) td.dma1(vdma, rv, (j + 1) * tile_bytes, wave, ks);
@@ -287,9 +306,9 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   // last tile: mask keys past the end, skip the empty half of the PV product
   f32x16 sl[2] = {odd ? sb[0] : sa[0], odd ? sb[1] : sa[1]};
   if (nv_last < FBN) mask_tail(sl, nv_last, h);
-  update_max<D>(sl, st.o, st.m, st.l, c);
+  update_max<D, ENT>(sl, st.o, st.m, st.l, st.w, c);
   bf16x8 pb[4];
-  probs(sl, pb, st.l, c, st.m);
+  probs<ENT>(sl, pb, st.l, st.w, c, st.m);
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
@@ -299,6 +318,12 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   asm volatile("" : "+v"(r));
   if (a.lse && h == 0 && row0 + r < Lq)
     a.lse[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = st.m + __builtin_amdgcn_logf(lsum);
+  if constexpr (ENT) {
+    // entropy in bits: log2 of the denominator minus the mean of (logit - max)
+    const float w = halves_sum(st.w);
+    if (h == 0 && row0 + r < Lq)
+      a.ent[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = __builtin_amdgcn_logf(lsum) - w / lsum;
+  }
   if constexpr (DELTA) {
     // delta of this lane's query row instead of O: the sum over channels of G
     // times O (fp32, before any rounding); register i of tile mt holds channel
@@ -370,7 +395,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
 // every barrier, so their MFMA and softmax phases stop overlapping.
 constexpr int kFlashWaves = 4;
 
-template <int D, bool OUT_F32, bool DELTA = false>
+template <int D, bool OUT_F32, bool DELTA = false, bool ENT = false>
 __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs a, int qtiles, int qrows, int nwg) {
   using T = SwTile<D>;
   __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
@@ -380,8 +405,8 @@ __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs 
   const int id = xcd_order(blockIdx.x, nwg);
   const int qt = id % qtiles;
   const int rest = id / qtiles;
-  flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1, v0,
-                                                v1, threadIdx.x);
+  flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1,
+                                                     v0, v1, threadIdx.x);
 }
 
 // ---------------------------------------------------------------- group
@@ -446,7 +471,7 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) qf[ks] = ld_bf16x8(ql + swoff<D>(r, 2 * ks + h));
 
-  const float c = a.scale_log2;
+  float c = a.scale_log2;
   f32x16 s[QT];
 #pragma unroll
   for (int t = 0; t < QT; ++t) {
@@ -454,6 +479,19 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
       s[t] = mma(ld_bf16x8(kl + swoff<D>(32 * t + (lane & 31), 2 * ks + h)), qf[ks], s[t]);
+  }
+  const int64_t rows_off = static_cast<int64_t>(hd) * (a.head_elems / D);
+  if (a.kbias) {
+    // logits in bits with the per-key bias added; the scale is then already applied
+    const float* kb = a.kbias + rows_off + base;
+#pragma unroll
+    for (int t = 0; t < QT; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = 32 * t + acc_key(i, h);
+        if (key < L) s[t][i] = fmaf(s[t][i], c, kb[key * rs]);
+      }
+    c = 1.f;
   }
   float mx = -INFINITY;
 #pragma unroll
@@ -464,13 +502,17 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
       mx = fmaxf(mx, s[t][i]);
     }
   mx = halves_max(mx) * c;
-  float l = 0.f;
+  // l: the softmax denominator; wsum: sum of p * (logit - max) in bits (for the entropy)
+  float l = 0.f, wsum = 0.f;
+  const bool want_ent = a.ent != nullptr;
 #pragma unroll
   for (int t = 0; t < QT; ++t)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      s[t][i] = fast_exp2(fmaf(s[t][i], c, -mx));
+      const float z = fmaf(s[t][i], c, -mx);
+      s[t][i] = fast_exp2(z);
       l += s[t][i];
+      if (want_ent && s[t][i] > 0.f) wsum = fmaf(s[t][i], z, wsum);
     }
   f32x16 o[D / 32];
 #pragma unroll
@@ -493,7 +535,11 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
   }
   const float lsum = halves_sum(l);
   const float inv = 1.f / lsum;
-  if (a.lse && h == 0 && r < a.Lq) a.lse[hd * (a.head_elems / D) + qbase + r * rs] = mx + __builtin_amdgcn_logf(lsum);
+  if (a.lse && h == 0 && r < a.Lq) a.lse[rows_off + qbase + r * rs] = mx + __builtin_amdgcn_logf(lsum);
+  if (want_ent) {
+    const float w = halves_sum(wsum);
+    if (h == 0 && r < a.Lq) a.ent[rows_off + qbase + r * rs] = __builtin_amdgcn_logf(lsum) - w * inv;
+  }
   if constexpr (OUT_F32) {
     store_out<D, true>(ro, r, rs, o, inv, lane);
   } else {
@@ -554,7 +600,7 @@ __global__ void __launch_bounds__(256) fused_reset(int* ctl, int n) {
 // one pass, O written directly.
 template <int D>
 __device__ __forceinline__ void group_wave(const GroupedArgs& a, int hd, int p, char* kl, char* vl,
-                                           const FlashOffsets<D>& fo, int lane) {
+                                           const FlashOffsets<D>& fo, int lane, bool poison) {
   constexpr int ROWB = D * 2, CPR = D / 8, RPI = 1024 / ROWB;
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
   const int64_t base = problem_base(a, p);
@@ -601,7 +647,15 @@ __device__ __forceinline__ void group_wave(const GroupedArgs& a, int hd, int p, 
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt) o[mt] = mma(v_operand<D>(vl, fo, mt, st), pb, o[mt]);
   }
-  store_out<D, false>(ro, lane & 31, rs, o, 1.f / halves_sum(l), lane);
+  // poison: the wait for this group's Y timed out, so its rows are written as NaN (a quiet
+  // NaN bit pattern the compiler cannot see through: kernels build without NaN semantics)
+  float inv = 1.f / halves_sum(l);
+  if (poison) {
+    uint32_t nan_bits = 0x7fc00000u;
+    asm volatile("" : "+v"(nan_bits));
+    inv = __uint_as_float(nan_bits);
+  }
+  store_out<D, false>(ro, lane & 31, rs, o, inv, lane);
 }
 
 template <int D>
@@ -612,6 +666,7 @@ __global__ void __launch_bounds__(FNT, 2) fused_kernel(FusedArgs f, int qtiles, 
   __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
   __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
   __shared__ int ticket;
+  __shared__ int timed_out;
 
   const int tid = threadIdx.x;
   // hardware XCD of this workgroup (HW_REG_XCC_ID, bits 3:0)
@@ -651,18 +706,21 @@ __global__ void __launch_bounds__(FNT, 2) fused_kernel(FusedArgs f, int qtiles, 
       const int key = hd * f.tiles + u;
       if (key != acquired) {
         if (tid == 0) {
-          int spins = 0;
+          int spins = 0, late = 0;
           while (__hip_atomic_load(ready + key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
             __builtin_amdgcn_s_sleep(8);
             if (++spins > (1 << 20)) {
               __hip_atomic_store(f.ctl + kCtlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              late = 1;
               break;
             }
           }
+          timed_out = late;
         }
         __syncthreads();  // Y is read below with device-coherent loads only
         acquired = key;
       }
+      const bool poison = timed_out != 0;
       const int w = otid >> 6;
       char* const lds_wave = w == 0 ? k0 : w == 1 ? k1 : w == 2 ? v0 : v1;
       const FlashOffsets<D> fo(w, otid & 63, f.s2.row_stride);
@@ -671,7 +729,7 @@ __global__ void __launch_bounds__(FNT, 2) fused_kernel(FusedArgs f, int qtiles, 
       for (int g = w; g < kFusedGroups; g += 4) {
         const int j = j0 + g;
         if (j >= f.b) break;
-        group_wave<D>(f.s2, hd, u * f.b + j, lds_wave, lds_wave + 32 * 2 * D, fo, otid & 63);
+        group_wave<D>(f.s2, hd, u * f.b + j, lds_wave, lds_wave + 32 * 2 * D, fo, otid & 63, poison);
       }
     }
   }
@@ -687,7 +745,7 @@ bool offsets_fit(const GroupedArgs& a, int pad_rows) {
   return (static_cast<int64_t>(a.L) + pad_rows) * a.row_stride * a.D * 4 < (int64_t{1} << 31);
 }
 
-template <int D, bool F32, bool DELTA = false>
+template <int D, bool F32, bool DELTA = false, bool ENT = false>
 hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   // query rows in units of one wave's 32, spread evenly over the fewest
   // tiles of at most kFlashWaves units (a 1560-row block: 49 units, 13 tiles
@@ -698,8 +756,8 @@ hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   const int qrows = 32 * ((units + qtiles - 1) / qtiles);
   const int64_t nwg = static_cast<int64_t>(qtiles) * a.problems * a.heads;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((flash_kernel<D, F32, DELTA>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0, s, a,
-                     qtiles, qrows, static_cast<int>(nwg));
+  hipLaunchKernelGGL((flash_kernel<D, F32, DELTA, ENT>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0,
+                     s, a, qtiles, qrows, static_cast<int>(nwg));
   return hipGetLastError();
 }
 
@@ -725,7 +783,10 @@ hipError_t launch_group_d(const GroupedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool flash_supported(const GroupedArgs& a) { return mfma_types_ok(a) && a.L > 128 && offsets_fit(a, FBN); }
+bool flash_supported(const GroupedArgs& a) {
+  return mfma_types_ok(a) && a.L > 128 && offsets_fit(a, FBN) && !a.kbias &&
+         !(a.ent && (a.delta || a.o_type != kBF16));
+}
 
 hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
   if (!flash_supported(a)) return hipErrorInvalidValue;
@@ -733,6 +794,8 @@ hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
     if (!a.dg) return hipErrorInvalidValue;
     return a.D == 128 ? launch_flash_t<128, true, true>(a, s) : launch_flash_t<64, true, true>(a, s);
   }
+  if (a.ent)  // entropies of the rows (bf16 output only)
+    return a.D == 128 ? launch_flash_t<128, false, false, true>(a, s) : launch_flash_t<64, false, false, true>(a, s);
   const bool f32 = a.o_type == kF32;
   if (a.D == 128) return f32 ? launch_flash_t<128, true>(a, s) : launch_flash_t<128, false>(a, s);
   return f32 ? launch_flash_t<64, true>(a, s) : launch_flash_t<64, false>(a, s);
@@ -745,6 +808,7 @@ bool fused_supported(const GroupedArgs& s1, const GroupedArgs& s2) {
 }
 
 int64_t fused_ctl_ints(int64_t heads, int64_t tiles) { return kCtlReady + heads * tiles; }
+int64_t fused_ctl_error_index() { return kCtlError; }
 
 hipError_t launch_fused(const FusedArgs& f, hipStream_t s) {
   if (!fused_supported(f.s1, f.s2) || !f.ctl) return hipErrorInvalidValue;

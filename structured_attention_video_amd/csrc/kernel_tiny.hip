@@ -111,6 +111,7 @@ __global__ void __launch_bounds__(256) tiny_kernel(GroupedArgs a, int64_t total)
 #pragma unroll
         for (int e = 0; e < 8; ++e) part = fmaf(q[e], k[j][e], part);
         s[j] = group_sum<LP>(part) * c;
+        if (a.kbias) s[j] += a.kbias[hd * (a.head_elems / D) + base + j * a.row_stride];
         mx = fmaxf(mx, s[j]);
       }
     }
@@ -147,7 +148,9 @@ hipError_t launch_tiny_d(const GroupedArgs& a, hipStream_t s) {
 
 }  // namespace
 
-bool tiny_supported(const GroupedArgs& a) { return (a.D == 64 || a.D == 128) && a.L >= 1 && a.L <= 8; }
+bool tiny_supported(const GroupedArgs& a) {
+  return (a.D == 64 || a.D == 128) && a.L >= 1 && a.L <= 8 && !a.ent;
+}
 
 hipError_t launch_tiny(const GroupedArgs& a, hipStream_t s) {
   if (!tiny_supported(a)) return hipErrorInvalidValue;

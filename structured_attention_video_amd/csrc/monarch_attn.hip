@@ -18,8 +18,8 @@ struct monarch_plan {
 
 namespace {
 
-constexpr uint32_t kKnownFlags =
-    MONARCH_FLAG_Y_FP32 | MONARCH_FLAG_ALLOW_UNALIGNED | MONARCH_FLAG_GENERIC | MONARCH_FLAG_FUSED;
+constexpr uint32_t kKnownFlags = MONARCH_FLAG_Y_FP32 | MONARCH_FLAG_ALLOW_UNALIGNED | MONARCH_FLAG_GENERIC |
+                                  MONARCH_FLAG_FUSED | MONARCH_FLAG_REFINE;
 
 
 size_t elem_bytes(int32_t dt) { return dt == MONARCH_FP32 ? 4 : 2; }
@@ -34,6 +34,20 @@ ElemType as_elem(int32_t dt) { return dt == MONARCH_FP32 ? kF32 : kBF16; }
 int64_t ctl_offset(const monarch_plan_info& p) { return (tensor_bytes(p, p.y_dtype) + 255) / 256 * 256; }
 
 int64_t align256(int64_t x) { return (x + 255) / 256 * 256; }
+
+// Refinement-step workspace: Y (y_dtype), the mixed keys Kbar (input dtype) and the
+// stage-1 row entropies (fp32), each section 256-aligned.
+struct RefineLayout {
+  int64_t y, kbar, ent, total;
+};
+RefineLayout refine_layout(const monarch_plan_info& p) {
+  RefineLayout l{};
+  l.y = 0;
+  l.kbar = align256(tensor_bytes(p, p.y_dtype));
+  l.ent = l.kbar + align256(tensor_bytes(p, p.dtype));
+  l.total = l.ent + align256(p.batch * p.heads * p.N * 4);
+  return l;
+}
 
 // Backward workspace: Y and dY (bf16), the stage-2 partial dQ and dK (fp32),
 // then per-row lse and delta of both stages (fp32), each section 256-aligned.
@@ -101,6 +115,16 @@ GroupedArgs stage2_args(const monarch_plan_info& p, const void* q, const void* k
   return a;
 }
 
+// Stand-in target of the refinement fields when a kernel is chosen at plan time:
+// the choice only tests them for null; no kernel is launched with it.
+float g_choice_marker = 0.f;
+
+GroupedArgs with_refine_fields(GroupedArgs a, bool ent, bool kbias) {
+  if (ent) a.ent = &g_choice_marker;
+  if (kbias) a.kbias = &g_choice_marker;
+  return a;
+}
+
 int32_t choose_kernel(const GroupedArgs& a, uint32_t flags) {
   if (!(flags & MONARCH_FLAG_GENERIC)) {
     if (tiny_supported(a)) return kKernelTiny;
@@ -120,7 +144,7 @@ hipError_t launch(int32_t kernel, const GroupedArgs& a, hipStream_t s) {
 }
 
 bool bwd_plan_ok(const monarch_plan_info& p) {
-  if (p.dtype != MONARCH_BF16 || (p.flags & MONARCH_FLAG_GENERIC)) return false;
+  if (p.dtype != MONARCH_BF16 || (p.flags & MONARCH_FLAG_GENERIC) || p.refine_steps) return false;
   const bool has1 = p.b > 1, has2 = p.m_tau > 1;
   if (has1 || !has2) {
     GroupedArgs a = stage1_args(p, nullptr, nullptr, nullptr, nullptr, MONARCH_BF16);
@@ -236,7 +260,10 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
   i.scale = scale != 0.f ? scale : 1.0f / sqrtf(static_cast<float>(head_dim));
   i.flags = flags;
   const bool has1 = b > 1, has2 = i.m_tau > 1;
+  i.refine_steps = (flags & MONARCH_FLAG_REFINE) && has1 && has2 ? 1 : 0;
+  i.fused_error_offset = -1;
   i.workspace_bytes = (has1 && has2) ? tensor_bytes(i, i.y_dtype) : 0;
+  if (i.refine_steps) i.workspace_bytes = refine_layout(i).total;
   i.flops_stage1 = has1 || !has2 ? 4 * BH * N * b * head_dim : 0;
   i.flops_stage2 = has2 ? 4 * BH * N * i.m_tau * head_dim : 0;
   // kernel choice is a function of the problem geometry only (no device query)
@@ -248,15 +275,16 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
   }
   if (has2) {
     GroupedArgs a = stage2_args(i, nullptr, nullptr, nullptr, has1 ? i.y_dtype : dtype, nullptr);
-    i.stage2_kernel = choose_kernel(a, flags);
+    i.stage2_kernel = choose_kernel(with_refine_fields(a, false, i.refine_steps > 0), flags);
   }
   i.fused = 0;
-  if ((flags & MONARCH_FLAG_FUSED) && !(flags & MONARCH_FLAG_GENERIC) && has1 && has2) {
+  if ((flags & MONARCH_FLAG_FUSED) && !(flags & MONARCH_FLAG_GENERIC) && has1 && has2 && !i.refine_steps) {
     const GroupedArgs a1 = stage1_args(i, nullptr, nullptr, nullptr, nullptr, i.y_dtype);
     const GroupedArgs a2 = stage2_args(i, nullptr, nullptr, nullptr, i.y_dtype, nullptr);
     if (fused_supported(a1, a2)) {
       i.fused = 1;
       i.workspace_bytes = ctl_offset(i) + fused_ctl_ints(BH, i.tiles) * static_cast<int64_t>(sizeof(int));
+      i.fused_error_offset = ctl_offset(i) + fused_ctl_error_index() * static_cast<int64_t>(sizeof(int));
     }
   }
   *out = p;
@@ -304,6 +332,23 @@ static monarch_status forward_launch(const monarch_plan_info& p, const void* q, 
   const bool has1 = p.b > 1, has2 = p.m_tau > 1;
   if (!has2) return run_stage1(p, q, k, v, o, p.dtype, s);  // second factor is the identity
   if (!has1) return run_stage2(p, q, k, v, p.dtype, o, s);  // first factor is the identity: Y = V
+  if (p.refine_steps) {
+    // one refinement step: Y = R V, Kbar = R K with the entropies of R's rows, then
+    // stage 2 against Kbar with the entropies as key biases
+    const RefineLayout lay = refine_layout(p);
+    char* w = static_cast<char*>(workspace);
+    void* y = w + lay.y;
+    void* kbar = w + lay.kbar;
+    float* ent = reinterpret_cast<float*>(w + lay.ent);
+    monarch_status st = run_stage1(p, q, k, v, y, p.y_dtype, s);
+    if (st != MONARCH_OK) return st;
+    GroupedArgs a1 = stage1_args(p, q, k, k, kbar, p.dtype);
+    a1.ent = ent;
+    if (launch(choose_kernel(a1, p.flags), a1, s) != hipSuccess) return MONARCH_ERR_HIP;
+    GroupedArgs a2 = stage2_args(p, q, kbar, y, p.y_dtype, o);
+    a2.kbias = ent;
+    return launch(p.stage2_kernel, a2, s) == hipSuccess ? MONARCH_OK : MONARCH_ERR_HIP;
+  }
   if (p.fused) {
     FusedArgs f{};
     f.s1 = stage1_args(p, q, k, v, workspace, p.y_dtype);
@@ -369,6 +414,7 @@ monarch_status monarch_attn_stage2(const monarch_plan* plan, const void* q, cons
   if (!plan || !q || !k || !y || !o) return MONARCH_ERR_INVALID_ARG;
   const monarch_plan_info& p = plan->info;
   if (p.m_tau == 1) return MONARCH_ERR_INVALID_ARG;
+  if (p.refine_steps) return MONARCH_ERR_UNSUPPORTED;  // needs the mixed keys and entropies
   if (misaligned(q) || misaligned(k) || misaligned(y) || misaligned(o)) return MONARCH_ERR_UNALIGNED;
   const int32_t ydt = p.b > 1 ? p.y_dtype : p.dtype;
   const int64_t io = tensor_bytes(p, p.dtype), ny = tensor_bytes(p, ydt);
@@ -381,6 +427,7 @@ monarch_status monarch_attn_chunk_forward(const monarch_plan* plan, int32_t t0, 
   if (!plan || !q || !k || !v || !o) return MONARCH_ERR_INVALID_ARG;
   const monarch_plan_info& p = plan->info;
   if (t0 < 0 || t1 <= t0 || t1 > p.T) return MONARCH_ERR_INVALID_ARG;
+  if (p.refine_steps) return MONARCH_ERR_UNSUPPORTED;
   const int64_t frame = p.H * p.W;
   // chunks must consist of whole blocks, and stage 2 must span the whole video
   if (p.tiles != 1 || frame % p.b != 0) return MONARCH_ERR_UNSUPPORTED;

@@ -29,7 +29,7 @@ def test_every_declared_symbol_is_exported():
     assert declared == set(_lib.EXPORTED)
     for name in declared:
         assert hasattr(L, name), name
-    assert L.monarch_attn_abi_version() == 4
+    assert L.monarch_attn_abi_version() == 5
 
 
 def _plan(batch=1, heads=2, d=128, grid=(4, 6, 10), align=0, custom_b=0, tile=0, dtype=0,
@@ -344,3 +344,53 @@ def test_chunk_forward_argument_errors():
         assert st == _lib.OK
         assert L.monarch_attn_chunk_forward(h, 0, 2, *ptr, None) == _lib.ERR_UNSUPPORTED
         L.monarch_attn_destroy(h)
+
+
+# ------------------------------------------------------------------ refinement step
+def test_refine_plan_info_and_workspace():
+    a256 = lambda x: (x + 255) // 256 * 256
+    info, ws = _info(heads=12, grid=(21, 30, 52), flags=_lib.FLAG_REFINE)
+    assert info.refine_steps == 1 and info.fused == 0 and info.fused_error_offset == -1
+    t = 12 * 32760 * 128 * 2
+    assert ws == a256(t) + a256(t) + a256(12 * 32760 * 4)      # Y, mixed keys, entropies
+    info, ws = _info(heads=2, grid=(4, 6, 10), flags=_lib.FLAG_REFINE | _lib.FLAG_Y_FP32)
+    assert ws == a256(2 * 240 * 128 * 4) + a256(2 * 240 * 128 * 2) + a256(2 * 240 * 4)
+    # the fused flag is overridden
+    info, _ = _info(heads=2, grid=(4, 6, 10), flags=_lib.FLAG_REFINE | _lib.FLAG_FUSED)
+    assert info.refine_steps == 1 and info.fused == 0
+    # nothing to refine with one factor the identity
+    for align in (2, 3):
+        info, ws = _info(heads=2, grid=(4, 6, 10), align=align, flags=_lib.FLAG_REFINE)
+        assert info.refine_steps == 0 and ws == 0
+
+
+def test_refine_stage2_kernel_supports_key_biases():
+    # m_tau = 3 (tiny), 4 (group) and 150 (> 128: generic) with key biases
+    info, _ = _info(heads=1, grid=(3, 5, 20), flags=_lib.FLAG_REFINE)
+    assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"tiny_group_valu"
+    info, _ = _info(heads=1, grid=(12, 5, 30), flags=_lib.FLAG_REFINE)
+    assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"small_group_mfma_bf16"
+    info, _ = _info(heads=1, grid=(10, 15, 8), align=1, flags=_lib.FLAG_REFINE)
+    assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"generic_valu_fp32"
+
+
+def test_refine_unsupported_entry_points():
+    st, h = _plan(heads=2, grid=(4, 6, 10), flags=_lib.FLAG_REFINE)
+    assert st == _lib.OK
+    assert L.monarch_attn_stage2(h, A, A + STEP, A + 2 * STEP, A + 3 * STEP, None) == _lib.ERR_UNSUPPORTED
+    assert L.monarch_attn_chunk_forward(h, 0, 2, A, A + STEP, A + 2 * STEP, A + 3 * STEP, A + 4 * STEP,
+                                        None) == _lib.ERR_UNSUPPORTED
+    assert L.monarch_attn_backward_workspace_size(h) == 0
+    assert L.monarch_attn_forward_train(h, A, A + STEP, A + 2 * STEP, A + 3 * STEP, A + 4 * STEP, 1 << 30,
+                                        None) == _lib.ERR_UNSUPPORTED
+    # the forward checks the larger workspace
+    ws = L.monarch_attn_workspace_size(h)
+    assert _fwd(h, ws_n=ws - 1) == _lib.ERR_WORKSPACE
+    L.monarch_attn_destroy(h)
+
+
+def test_fused_error_offset():
+    info, ws = _info(heads=12, grid=(21, 30, 52), flags=_lib.FLAG_FUSED)
+    y = 12 * 32760 * 128 * 2
+    assert info.fused == 1 and info.fused_error_offset == (y + 255) // 256 * 256 + 8 * 4
+    assert info.fused_error_offset + 4 <= ws
