@@ -59,6 +59,14 @@ def parse():
                          "never (off, the default: the two-launch path measures faster)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (for HBM counter scaling)")
+    ap.add_argument("--settle-s", type=float, default=0.3,
+                    help="seconds of untimed forward calls before the warm-up calls (the first ~10 ms of "
+                         "load after idle run in a power-management transient)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="only summarise a rocprofv3 kernel-trace CSV of a run of this bench (no GPU): "
+                         "per-kernel launch statistics and the dominant kernel's roofline fraction")
+    ap.add_argument("--trace-kernel", default="flash_kernel<128, false, false>",
+                    help="with --trace-summary: substring of the stage-1 kernel's name")
     return ap.parse_args()
 
 
@@ -89,6 +97,57 @@ def stored_traffic(kernel: str, config: str):
         return float(kv["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def trace_summary(path: str, config: str, kernel: str) -> None:
+    """Per-kernel statistics of a rocprofv3 --kernel-trace CSV of a run of this bench, and the
+    roofline fraction of the stage-1 kernel at this workload from its mean launch duration.
+    Launches are grouped by kernel and grid size (the dense comparison and the chunk use the
+    same kernel on other grids); the stage-1 group is the most-launched one whose kernel name
+    contains `kernel`, and its mean is over every launch in it."""
+    import csv
+    import statistics
+    import datagen
+    c = datagen.CONFIGS[config]
+    T, H, W = c["grid"]
+    N = T * H * W
+    b = {"frame": H * W, "row": W, "dense": N, "token": 1}[c["align"]]
+    flops1 = 4 * c["batch"] * c["heads"] * N * b * c["d"]
+    rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]))
+        by.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"# {os.path.basename(path)}: {len(rows)} dispatches; durations in us")
+    print(f"{'calls':>5} {'mean':>9} {'median':>9} {'min':>9} {'max':>9} {'threads':>9}  kernel")
+    for (name, grid), d in sorted(by.items(), key=lambda kv: -sum(kv[1])):
+        print(f"{len(d):5d} {statistics.mean(d):9.1f} {statistics.median(d):9.1f} {min(d):9.1f} {max(d):9.1f} "
+              f"{grid:9d}  {name[:90]}")
+    cand = [(k, d) for k, d in by.items() if kernel in k[0]]
+    if not cand:
+        print(f"# no kernel matching {kernel!r}")
+        return
+    (name, grid), d = max(cand, key=lambda kv: len(kv[1]))
+    mean = statistics.mean(d)
+    tf = flops1 / (mean * 1e-6) / 1e12
+    print(f"# stage-1 kernel {name[:70]} (grid {grid} threads): {len(d)} launches, mean {mean:.1f} us, "
+          f"median {statistics.median(d):.1f} us")
+    print(f"# stage-1 algorithmic FLOP per launch {flops1} / mean -> {tf:.1f} TFLOP/s = frac "
+          f"{tf / PEAK_BF16_TFLOPS:.4f} of {PEAK_BF16_TFLOPS:.0f} TFLOP/s")
+
+
+def settle(fn, seconds: float) -> int:
+    """Untimed calls of fn for about `seconds` of wall time; returns how many."""
+    import torch
+    if seconds <= 0:
+        return 0
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds and n < 100000:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    return n
 
 
 def copy_calibration():
@@ -142,6 +201,10 @@ def main():
                           "sharded across GPUs (see the multi-GPU design note)", "n_gpus": args.gpus}))
         sys.exit(2)
 
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.config, args.trace_kernel)
+        return
+
     import torch
     import datagen
     from structured_attention_video_amd import MonarchPlan
@@ -187,6 +250,10 @@ def main():
         torch.cuda.synchronize()
         return sorted(e[0].elapsed_time(e[1]) for e in ev)
 
+    # The first ~10 ms of load after idle run in a power-management transient (launches up
+    # to ~30% slower, then back to the sustained rate): settle first, untimed, so that the
+    # warm-up and the timed calls see the sustained clock.
+    settle_calls = settle(call, args.settle_s)
     for _ in range(args.warmup):
         call()
     # the timed region: exactly `steps` calls, nothing else enqueued between them
@@ -272,6 +339,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_calls": settle_calls,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
