@@ -14,7 +14,8 @@ Prints ONE JSON line. Besides the contract fields it carries:
                 then stage 2), timed separately; dense: the library's own
                 dense softmax-attention kernel at the same shape; backward:
                 the gradient pass at the same shape; chunk: one frame-causal
-                chunk of three frames after a cache of the earlier frames.
+                chunk of three frames after a cache of the earlier frames;
+                refine_one_step: the forward with one refinement step.
 A call is stage 1 then stage 2 (two launches); --fused auto/on times the
 library's one-launch fused variant instead where it applies (frame and tiled
 alignments). call_ms_events: per-call device time from HIP events in a second
@@ -65,8 +66,14 @@ def parse():
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="only summarise a rocprofv3 kernel-trace CSV of a run of this bench (no GPU): "
                          "per-kernel launch statistics and the dominant kernel's roofline fraction")
-    ap.add_argument("--trace-kernel", default="flash_kernel<128, false, false>",
-                    help="with --trace-summary: substring of the stage-1 kernel's name")
+    ap.add_argument("--trace-kernel", default="flash_kernel<128, false, false",
+                    help="with --trace-summary / --traffic-summary: substring of the kernel's name")
+    ap.add_argument("--counter-summary", nargs="+", metavar="CSV",
+                    help="only summarise rocprofv3 --pmc CSVs (no GPU): per kernel and grid, the mean of "
+                         "every counter over its dispatches")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="only summarise HBM traffic (no GPU) from four rocprofv3 --pmc CSVs: FETCH_SIZE and "
+                         "WRITE_SIZE of a run of this bench, and of a --copy-calibration run")
     return ap.parse_args()
 
 
@@ -136,6 +143,54 @@ def trace_summary(path: str, config: str, kernel: str) -> None:
           f"{tf / PEAK_BF16_TFLOPS:.4f} of {PEAK_BF16_TFLOPS:.0f} TFLOP/s")
 
 
+def _pmc_rows(path):
+    import csv
+    by = {}
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], int(r.get("Grid_Size") or r.get("Grid_Size_X") or 0))
+        d = by.setdefault(key, {})
+        d.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    return by
+
+
+def counter_summary(paths) -> None:
+    """Mean of every counter per (kernel, grid size) over its dispatches, per CSV."""
+    for path in paths:
+        print(f"# {os.path.basename(os.path.dirname(path))}/{os.path.basename(path)}")
+        for (name, grid), d in sorted(_pmc_rows(path).items(), key=lambda kv: kv[0]):
+            vals = ", ".join(f"{k}={sum(v) / len(v):.4g}" for k, v in sorted(d.items()))
+            n = max(len(v) for v in d.values())
+            print(f"{name[:70]:70s} grid={grid:<8d} dispatches={n:<4d} {vals}")
+
+
+def traffic_summary(paths, config: str, kernel: str) -> None:
+    """HBM bytes per launch of the kernels of a bench run: FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch) scaled by what the same counters read for a plain device copy of known size."""
+    fetch, write, cfetch, cwrite = (_pmc_rows(p) for p in paths)
+    copy_bytes = 1 << 30
+
+    def one(rows, counter):
+        vals = [v for d in rows.values() for v in d.get(counter, [])]
+        return max(vals) if vals else float("nan")
+    f_copy = copy_bytes / (one(cfetch, "FETCH_SIZE") * 1024)
+    w_copy = copy_bytes / (one(cwrite, "WRITE_SIZE") * 1024)
+    print(f"# copy calibration ({copy_bytes} B read and written): FETCH_SIZE factor {f_copy:.3f}, "
+          f"WRITE_SIZE factor {w_copy:.3f}")
+    print(f"source_digest: {source_digest()}")
+    for (name, grid), d in sorted(fetch.items(), key=lambda kv: kv[0]):
+        fv = d.get("FETCH_SIZE", [])
+        wv = write.get((name, grid), {}).get("WRITE_SIZE", [])
+        if not fv or not wv:
+            continue
+        fb = sum(fv) / len(fv) * 1024 * f_copy
+        wb = sum(wv) / len(wv) * 1024 * w_copy
+        tag = "  <- hbm_bytes_per_launch" if kernel in name else ""
+        print(f"# {name[:70]} grid={grid}: read {fb:.4g} B, written {wb:.4g} B per launch{tag}")
+        if tag:
+            print(f"hbm_bytes_per_launch: {fb + wb:.6g}")
+            tag = ""
+
+
 def settle(fn, seconds: float) -> int:
     """Untimed calls of fn for about `seconds` of wall time; returns how many."""
     import torch
@@ -203,6 +258,12 @@ def main():
 
     if args.trace_summary:
         trace_summary(args.trace_summary, args.config, args.trace_kernel)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary, args.config, args.trace_kernel)
         return
 
     import torch
@@ -374,6 +435,21 @@ def main():
                                 "bitwise_equal_to_timed_output": bool(torch.equal(oa, o))}
         del oa, alt_ws
     alt.close()
+
+    # the forward with one refinement step of the factors at the same shape, for context
+    rplan = MonarchPlan(c["batch"], c["heads"], c["d"], c["grid"], align=c["align"],
+                        tile_tokens=c["tile_tokens"], dtype=dt, refine=True)
+    if rplan.info["refine_steps"] and not args.forward_only:
+        rws = rplan.new_workspace(dev)
+        orf = torch.empty_like(q)
+        for _ in range(2):
+            rplan.forward(q, k, v, out=orf, workspace=rws)
+        tr = timed(lambda: rplan.forward(q, k, v, out=orf, workspace=rws), args.steps)
+        k1r, k2r = rplan.kernel_names()
+        out["refine_one_step"] = {"ms_per_call_p50": round(pct(tr, 0.5), 4),
+                                  "kernels": [k1r, k1r, k2r], "launches": "Y = R V; R K with row entropies; stage 2"}
+        del rws, orf
+    rplan.close()
 
     # the backward pass (gradients of all three inputs) at the same shape, for context:
     # time per call and the rate at 2.5x the forward FLOPs (five products of the

@@ -84,7 +84,7 @@ __device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const F
 // slice of the exponentials; sched_barrier keeps the steps apart so the
 // compiler does not regroup all MFMAs first. hook(ks) runs after step ks's
 // MFMAs are issued (the caller's tile copies go there).
-template <int D, bool ENT, typename Hook>
+template <int D, bool ENT, bool PIN, typename Hook>
 __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* kl, const FlashOffsets<D>& fo,
                                                   const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
                                                   bf16x8 (&pb)[4], float& l, float& w, float c, float m,
@@ -117,6 +117,11 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
         if (p0 > 0.f) w = fmaf(p0, z0, w);
         if (p1 > 0.f) w = fmaf(p1, z1, w);
       }
+      // pin the weights to this step: without it the compiler sinks every
+      // exponential of the tile below the last score MFMA in one of the two
+      // unrolled steps, and that step loses its MFMA/VALU overlap (left out
+      // where the extra register pressure would spill)
+      if constexpr (PIN) asm volatile("" : "+v"(pp[i >> 1]));
     }
     __builtin_amdgcn_sched_barrier(0);
     a0 = n0;
@@ -273,7 +278,9 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
       // the wave's copy instructions go one per score step (V's first, then
       // K's) instead of back to back before them: stage 1 at the frame shape
       // measured 1.7% faster
-      scores_with_probs<D, ENT>(sn, kread, fo, qf, s, pb, st.l, st.w, c, st.m, [&](int ks) {
+      scores_with_probs<D, ENT, !ENT && !OUT_F32 && !DELTA && POLICY == 0>(sn, kread, fo, qf, s, pb, st.l, st.w, c,
+                                                                            st.m,
+                                                            [&](int ks) {
         constexpr int IPW = TileDma<D, NW>::IPW;
         static_assert(2 * IPW <= D / 16, "one copy instruction per score step");
         if (ks < IPW) td.dma1(vdma, rv, (j + 1) * tile_bytes, wave, ks);
