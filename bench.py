@@ -78,11 +78,12 @@ def parse():
 
 
 def source_digest() -> str:
-    """Digest of the kernel sources; stored HBM counter figures are valid only for it."""
+    """Digest of the device-code sources (kernel_*.hip and the headers they include; not the
+    host-only C-ABI source); stored HBM counter figures are valid only for it."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "structured_attention_video_amd", "csrc")
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".h")):
+        if f.endswith(".h") or (f.startswith("kernel_") and f.endswith(".hip")):
             h.update(f.encode())
             h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
@@ -119,7 +120,11 @@ def trace_summary(path: str, config: str, kernel: str) -> None:
     T, H, W = c["grid"]
     N = T * H * W
     b = {"frame": H * W, "row": W, "dense": N, "token": 1}[c["align"]]
-    flops1 = 4 * c["batch"] * c["heads"] * N * b * c["d"]
+    m = (c["tile_tokens"] or N) // b
+    # the MFMA flash kernel takes the stage whose problems exceed 128 rows (stage 1: b rows,
+    # stage 2: m_tau rows); its algorithmic FLOP per launch are that stage's
+    stage, L = ("stage-1", b) if b > 128 else ("stage-2", m)
+    flops1 = 4 * c["batch"] * c["heads"] * N * L * c["d"]
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
     by = {}
     for r in rows:
@@ -137,9 +142,9 @@ def trace_summary(path: str, config: str, kernel: str) -> None:
     (name, grid), d = max(cand, key=lambda kv: len(kv[1]))
     mean = statistics.mean(d)
     tf = flops1 / (mean * 1e-6) / 1e12
-    print(f"# stage-1 kernel {name[:70]} (grid {grid} threads): {len(d)} launches, mean {mean:.1f} us, "
+    print(f"# {stage} kernel {name[:70]} (grid {grid} threads): {len(d)} launches, mean {mean:.1f} us, "
           f"median {statistics.median(d):.1f} us")
-    print(f"# stage-1 algorithmic FLOP per launch {flops1} / mean -> {tf:.1f} TFLOP/s = frac "
+    print(f"# {stage} algorithmic FLOP per launch {flops1} / mean -> {tf:.1f} TFLOP/s = frac "
           f"{tf / PEAK_BF16_TFLOPS:.4f} of {PEAK_BF16_TFLOPS:.0f} TFLOP/s")
 
 

@@ -247,8 +247,10 @@ monarch_status monarch_attn_backward_saved(const monarch_plan* plan, const void*
                                            const void* o, const void* grad_o, void* grad_q, void* grad_k,
                                            void* grad_v, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Static description of a status code (never NULL). */
-const char* monarch_status_string(monarch_status status);
+/* Static description of a status code (never NULL; "unknown status" for a value
+ * that is no monarch_status). The code is taken as a plain integer so that any
+ * value is well defined to pass. */
+const char* monarch_status_string(int32_t status);
 
 /* Static name of a kernel variant id from monarch_plan_info (never NULL). */
 const char* monarch_attn_kernel_name(int32_t kernel_id);

@@ -656,7 +656,7 @@ monarch_status monarch_attn_backward_saved(const monarch_plan* plan, const void*
   return backward_impl(plan, q, k, v, o, grad_o, grad_q, grad_k, grad_v, workspace, workspace_bytes, stream, true);
 }
 
-const char* monarch_status_string(monarch_status status) {
+const char* monarch_status_string(int32_t status) {
   switch (status) {
     case MONARCH_OK: return "ok";
     case MONARCH_ERR_INVALID_ARG: return "invalid argument";

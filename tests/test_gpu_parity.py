@@ -162,18 +162,26 @@ def test_full_size_workloads(name):
     assert_close(to_np(got), want, BF16, name)
 
 
-def test_long_video_sampled_groups():
+def test_long_video_all_heads():
+    """The long workload (81 frames, N = 126360) on all 12 heads, every element."""
     c = datagen.CONFIGS["long_bf16"]
     q, k, v = datagen.config_inputs("long_bf16")
     got = run(q, k, v, c["grid"], "frame")
-    rng = np.random.default_rng(5)
-    heads = [0, 7, 11]
-    groups = [(0, int(j)) for j in np.concatenate([[0, 1, 1559], rng.integers(0, 1560, 21)])]
-    res = oracle.monarch_forward_groups(q[0], k[0], v[0], 1560, None, None, heads, groups)
-    gq = to_np(got)[0]
-    g = np.concatenate([gq[h, idx] for (h, u, j), (idx, _) in res.items()])
-    w = np.concatenate([rows for (idx, rows) in res.values()])
-    assert_close(g, w, BF16, "long video, sampled groups")
+    b = oracle.block_size(c["grid"], "frame")
+    for h in range(q.shape[1]):
+        want = ref(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], b)
+        assert_close(to_np(got)[:, h:h + 1], want, BF16, f"long video head {h}")
+
+
+def test_long_dense_kernel_sampled_rows():
+    """The dense kernel (b = N) at the long shape on sampled rows, including both ends."""
+    c = datagen.CONFIGS["long_bf16"]
+    q, k, v = datagen.config_inputs("long_bf16", heads=1)
+    got = run(q, k, v, c["grid"], "dense")
+    N = q.shape[2]
+    rows = np.concatenate([[0, 1, N - 2, N - 1], np.random.default_rng(8).integers(0, N, 60)])
+    want = oracle.dense_attention(q[0, 0], k[0, 0], v[0, 0], rows=rows)
+    assert_close(to_np(got)[0, 0, rows], want, BF16, "long dense head 0")
 
 
 def test_dense_kernel_sampled_rows():
