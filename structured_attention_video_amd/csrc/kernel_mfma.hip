@@ -182,6 +182,31 @@ __device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vl, const 
   }
 }
 
+// Key biases (refinement step): the 64 biases of a key tile (bits, fp32) come
+// into LDS beside the tile's values, one 4-byte copy per lane issued by wave 0;
+// each lane then turns its raw scores into logits in bits, c s + bias, for its
+// keys 32 t + acc_key(i, h) (four consecutive keys per 16-byte read).
+__device__ __forceinline__ void lds_dma4(__amdgpu_buffer_rsrc_t src, float* lds, uint32_t voff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, (lds_void*)lds, 4, voff, 0, 0, 0);
+#else
+  (void)src; (void)lds; (void)voff;
+#endif
+}
+
+__device__ __forceinline__ void add_kbias(f32x16 (&s)[2], const float* kb, int h, float c) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 b = *reinterpret_cast<const float4*>(kb + 32 * t + 8 * g + 4 * h);
+      s[t][4 * g + 0] = fmaf(s[t][4 * g + 0], c, b.x);
+      s[t][4 * g + 1] = fmaf(s[t][4 * g + 1], c, b.y);
+      s[t][4 * g + 2] = fmaf(s[t][4 * g + 2], c, b.z);
+      s[t][4 * g + 3] = fmaf(s[t][4 * g + 3], c, b.w);
+    }
+}
+
 // Wave priority while issuing MFMA-heavy phases (MONARCH_PRIO): 0 = never
 // raised; 1 = raised for the value product; 2 = raised for scores + values
 // (measured best: the two waves sharing a SIMD then tend to alternate
@@ -209,9 +234,13 @@ struct FlashState {
 // the barriers. Every copy it issues has completed when it returns; waves
 // whose rows lie outside the tile or past the end of the problem only copy,
 // and return early (after the last barrier).
-template <int D, bool OUT_F32, int POLICY = 0, int NW = 4, bool DELTA = false, bool ENT = false>
+//
+// KB (key biases, bf16 output only): logits are c <q, k> + kbias[key] in bits;
+// kb0 / kb1 are two 64-float LDS slots that alternate like v0 / v1.
+template <int D, bool OUT_F32, int POLICY = 0, int NW = 4, bool DELTA = false, bool ENT = false, bool KB = false>
 __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, int qt, int qrows, char* k0,
-                                           char* k1, char* v0, char* v1, int tid) {
+                                           char* k1, char* v0, char* v1, int tid, float* kb0 = nullptr,
+                                           float* kb1 = nullptr) {
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
   const int64_t base = problem_base(a, p);
   const int64_t rs = a.row_stride;
@@ -232,13 +261,23 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   const int n = (L + FBN - 1) / FBN;
   const int nv_last = L - (n - 1) * FBN;
   const float c = a.scale_log2;
+  // with key biases the scores are logits in bits once the biases are added,
+  // so the softmax below runs with scale 1
+  const float cs = KB ? 1.f : c;
   const FlashOffsets<D> fo(wave, lane, rs);  // LDS read offsets
   const TileDma<D, NW> td(wave, lane, rs);
   const uint32_t tile_bytes = static_cast<uint32_t>(FBN * rs * D * 2);
+  const auto rb = problem_rsrc(KB ? static_cast<const void*>(a.kbias + hd * (a.head_elems / D)) : a.k, base, rs,
+                               L, 1, 4);  // key biases (unused without KB)
+  const uint32_t kb_lane = static_cast<uint32_t>(lane * rs * 4);
+  const uint32_t kb_tile = static_cast<uint32_t>(FBN * rs * 4);
 
-  // prologue: K tiles 0 and 1, V tile 0
+  // prologue: K tiles 0 and 1, V tile 0 (and its key biases)
   td.dma(k0, rk, 0, wave);
   td.dma(v0, rv, 0, wave);
+  if constexpr (KB) {
+    if (wave == 0) lds_dma4(rb, kb0, kb_lane);
+  }
   if (n > 1) td.dma(k1, rk, tile_bytes, wave);
   bf16x8 qf[D / 16];
   load_qfrag<D>(qf, rq, row0, rs, lane);
@@ -262,15 +301,19 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   // vread. The four LDS slots are distinct fields so the compiler can see
   // that the reads never touch the tiles being copied and does not wait for
   // the copies first.
-  auto step = [&](int j, char* kdma, char* vdma, const char* kread, const char* vread, const f32x16 (&s)[2],
-                  f32x16 (&sn)[2]) {
+  auto step = [&](int j, char* kdma, char* vdma, const char* kread, const char* vread, float* kbdma,
+                  const float* kbread, f32x16 (&s)[2], f32x16 (&sn)[2]) {
     // copies of V_{j+1} and K_{j+2}: waves without rows issue them here,
     // the others between their score steps (below)
     const bool kc = j + 2 < n;
+    if constexpr (KB) {
+      if (wave == 0) lds_dma4(rb, kbdma, (j + 1) * kb_tile + kb_lane);
+    }
     if (!active) td.dma(vdma, rv, (j + 1) * tile_bytes, wave);
     if (!active && kc) td.dma(kdma, rk, (j + 2) * tile_bytes, wave);
     if (active) {
-      update_max<D, ENT>(s, st.o, st.m, st.l, st.w, c);
+      if constexpr (KB) add_kbias(s, kbread, h, c);
+      update_max<D, ENT>(s, st.o, st.m, st.l, st.w, cs);
       bf16x8 pb[4];
 #if MONARCH_PRIO == 2
       __builtin_amdgcn_s_setprio(1);
@@ -278,7 +321,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
       // the wave's copy instructions go one per score step (V's first, then
       // K's) instead of back to back before them: stage 1 at the frame shape
       // measured 1.7% faster
-      scores_with_probs<D, ENT, !ENT && !OUT_F32 && !DELTA && POLICY == 0>(sn, kread, fo, qf, s, pb, st.l, st.w, c,
+      scores_with_probs<D, ENT, !ENT && !OUT_F32 && !DELTA && !KB && POLICY == 0>(sn, kread, fo, qf, s, pb, st.l, st.w, cs,
                                                                             st.m,
                                                             [&](int ks) {
         constexpr int IPW = TileDma<D, NW>::IPW;
@@ -303,19 +346,20 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   // the reverse
   int j = 0;
   for (; j + 2 < n; j += 2) {
-    step(j, k0, v1, k1, v0, sa, sb);
-    step(j + 1, k1, v0, k0, v1, sb, sa);
+    step(j, k0, v1, k1, v0, kb1, kb0, sa, sb);
+    step(j + 1, k1, v0, k0, v1, kb0, kb1, sb, sa);
   }
   const bool odd = j + 1 < n;
-  if (odd) step(j, k0, v1, k1, v0, sa, sb);
+  if (odd) step(j, k0, v1, k1, v0, kb1, kb0, sa, sb);
 
   if (!active) return;
   // last tile: mask keys past the end, skip the empty half of the PV product
   f32x16 sl[2] = {odd ? sb[0] : sa[0], odd ? sb[1] : sa[1]};
+  if constexpr (KB) add_kbias(sl, ((n - 1) & 1) ? kb1 : kb0, h, c);
   if (nv_last < FBN) mask_tail(sl, nv_last, h);
-  update_max<D, ENT>(sl, st.o, st.m, st.l, st.w, c);
+  update_max<D, ENT>(sl, st.o, st.m, st.l, st.w, cs);
   bf16x8 pb[4];
-  probs<ENT>(sl, pb, st.l, st.w, c, st.m);
+  probs<ENT>(sl, pb, st.l, st.w, cs, st.m);
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
@@ -402,7 +446,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
 // every barrier, so their MFMA and softmax phases stop overlapping.
 constexpr int kFlashWaves = 4;
 
-template <int D, bool OUT_F32, bool DELTA = false, bool ENT = false>
+template <int D, bool OUT_F32, bool DELTA = false, bool ENT = false, bool KB = false>
 __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs a, int qtiles, int qrows, int nwg) {
   using T = SwTile<D>;
   __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
@@ -412,8 +456,15 @@ __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs 
   const int id = xcd_order(blockIdx.x, nwg);
   const int qt = id % qtiles;
   const int rest = id / qtiles;
-  flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1,
-                                                     v0, v1, threadIdx.x);
+  if constexpr (KB) {
+    __shared__ __attribute__((aligned(256))) float kb0[FBN];
+    __shared__ __attribute__((aligned(256))) float kb1[FBN];
+    flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT, true>(a, rest / a.problems, rest % a.problems, qt, qrows, k0,
+                                                             k1, v0, v1, threadIdx.x, kb0, kb1);
+  } else {
+    flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1,
+                                                       v0, v1, threadIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------- group
@@ -752,7 +803,7 @@ bool offsets_fit(const GroupedArgs& a, int pad_rows) {
   return (static_cast<int64_t>(a.L) + pad_rows) * a.row_stride * a.D * 4 < (int64_t{1} << 31);
 }
 
-template <int D, bool F32, bool DELTA = false, bool ENT = false>
+template <int D, bool F32, bool DELTA = false, bool ENT = false, bool KB = false>
 hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   // query rows in units of one wave's 32, spread evenly over the fewest
   // tiles of at most kFlashWaves units (a 1560-row block: 49 units, 13 tiles
@@ -763,7 +814,7 @@ hipError_t launch_flash_t(const GroupedArgs& a, hipStream_t s) {
   const int qrows = 32 * ((units + qtiles - 1) / qtiles);
   const int64_t nwg = static_cast<int64_t>(qtiles) * a.problems * a.heads;
   if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((flash_kernel<D, F32, DELTA, ENT>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0,
+  hipLaunchKernelGGL((flash_kernel<D, F32, DELTA, ENT, KB>), dim3(static_cast<unsigned>(nwg)), dim3(64 * kFlashWaves), 0,
                      s, a, qtiles, qrows, static_cast<int>(nwg));
   return hipGetLastError();
 }
@@ -791,8 +842,8 @@ hipError_t launch_group_d(const GroupedArgs& a, hipStream_t s) {
 }  // namespace
 
 bool flash_supported(const GroupedArgs& a) {
-  return mfma_types_ok(a) && a.L > 128 && offsets_fit(a, FBN) && !a.kbias &&
-         !(a.ent && (a.delta || a.o_type != kBF16));
+  return mfma_types_ok(a) && a.L > 128 && offsets_fit(a, FBN) &&
+         !(a.kbias && (a.ent || a.delta || a.o_type != kBF16)) && !(a.ent && (a.delta || a.o_type != kBF16));
 }
 
 hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
@@ -801,6 +852,9 @@ hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
     if (!a.dg) return hipErrorInvalidValue;
     return a.D == 128 ? launch_flash_t<128, true, true>(a, s) : launch_flash_t<64, true, true>(a, s);
   }
+  if (a.kbias)  // per-key biases of the logits (bf16 output only)
+    return a.D == 128 ? launch_flash_t<128, false, false, false, true>(a, s)
+                      : launch_flash_t<64, false, false, false, true>(a, s);
   if (a.ent)  // entropies of the rows (bf16 output only)
     return a.D == 128 ? launch_flash_t<128, false, false, true>(a, s) : launch_flash_t<64, false, false, true>(a, s);
   const bool f32 = a.o_type == kF32;

@@ -365,12 +365,17 @@ def test_refine_plan_info_and_workspace():
 
 
 def test_refine_stage2_kernel_supports_key_biases():
-    # m_tau = 3 (tiny), 4 (group) and 150 (> 128: generic) with key biases
+    # m_tau = 3 (tiny), 12 (group) and 150 (> 128: flash) with key biases; fp32 and the
+    # generic flag take the generic kernel
     info, _ = _info(heads=1, grid=(3, 5, 20), flags=_lib.FLAG_REFINE)
     assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"tiny_group_valu"
     info, _ = _info(heads=1, grid=(12, 5, 30), flags=_lib.FLAG_REFINE)
     assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"small_group_mfma_bf16"
     info, _ = _info(heads=1, grid=(10, 15, 8), align=1, flags=_lib.FLAG_REFINE)
+    assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"flash_mfma_bf16"
+    info, _ = _info(heads=1, grid=(10, 15, 8), align=1, dtype=1, flags=_lib.FLAG_REFINE)
+    assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"generic_valu_fp32"
+    info, _ = _info(heads=1, grid=(10, 15, 8), align=1, flags=_lib.FLAG_REFINE | _lib.FLAG_GENERIC)
     assert L.monarch_attn_kernel_name(info.stage2_kernel) == b"generic_valu_fp32"
 
 

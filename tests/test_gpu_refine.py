@@ -40,7 +40,9 @@ SMALL = [
     ((12, 5, 30), 128, BF16, "frame", 0, 0),    # b=150, m=12 (group kernel stage 2 with key biases)
     ((40, 3, 50), 128, BF16, "frame", 0, 0),    # b=150, m=40: two 32-row waves in stage 2
     ((5, 4, 37), 128, BF16, "row", 0, 0),       # b=37, m=20
-    ((10, 15, 8), 128, BF16, "row", 0, 0),      # b=8, m=150 > 128 (generic stage 2 with key biases)
+    ((10, 15, 8), 128, BF16, "row", 0, 0),      # b=8, m=150 > 128 (flash stage 2 with key biases, 22-key last tile)
+    ((20, 10, 6), 128, BF16, "row", 0, 0),      # b=6, m=200: four key tiles, 8 keys in the last
+    ((9, 20, 6), 64, BF16, "row", 0, 0),        # d=64, b=6, m=180 (flash stage 2, d=64)
     ((6, 7, 13), 64, BF16, "frame", 0, 0),      # d=64, b=91
     ((6, 7, 40), 64, BF16, "frame", 0, 0),      # d=64, b=280 (flash, d=64)
     ((6, 4, 25), 128, BF16, "frame", 200, 0),   # tiled: m_tau=2, 3 tiles
@@ -65,11 +67,12 @@ def test_refine_small_cases(grid, d, dtype, align, tile, cb):
     assert np.abs(want - direct).max() > 1e-3
 
 
-def test_refine_generic_kernels():
-    grid = (5, 4, 37)
+@pytest.mark.parametrize("grid,align", [((5, 4, 37), "frame"), ((10, 15, 8), "row")])
+def test_refine_generic_kernels(grid, align):
     q, k, v = datagen.qkv(1, 2, grid, 128, (54, 55, 56), dtype=BF16)
-    got = run(q, k, v, grid, "frame", generic=True)
-    assert_close(to_np(got), oracle.monarch_refine_forward(q, k, v, 148), BF16, "refine generic")
+    got = run(q, k, v, grid, align, generic=True)
+    b = oracle.block_size(grid, align)
+    assert_close(to_np(got), oracle.monarch_refine_forward(q, k, v, b), BF16, f"refine generic {align}")
 
 
 @pytest.mark.parametrize("align", ["dense", "token"])
@@ -86,7 +89,7 @@ def test_refine_degenerate_equals_direct(align):
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["frame_bf16", "tiled_bf16"])
+@pytest.mark.parametrize("name", ["frame_bf16", "row_bf16", "tiled_bf16"])
 def test_refine_full_size(name):
     c = datagen.CONFIGS[name]
     q, k, v = datagen.config_inputs(name)
