@@ -43,8 +43,9 @@ struct GroupedArgs {
   const void* dg;     // optional, flash kernel only, with delta: bf16 rows G (layout of q);
   float* delta;       // then, instead of O, delta[row] = sum over channels of G * O with O in
                       // fp32 before any rounding, indexed [head][token] (o is not written)
-  float* ent;         // optional (flash, group and generic kernels): per query row, the
-                      // Shannon entropy in bits of the row's softmax weights, [head][token]
+  float* ent;         // optional (flash when the values are the keys, group and generic
+                      // kernels): per query row, the Shannon entropy in bits of the row's
+                      // softmax weights, [head][token]
   const float* kbias; // optional (flash with bf16 output, group, tiny and generic kernels): per key row, a bias in
                       // bits added to the row's logits, i.e. weights ~ exp2(scale_log2 * <q,k>
                       // + kbias[key]); indexed [head][token]

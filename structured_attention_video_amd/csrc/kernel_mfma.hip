@@ -32,9 +32,8 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(
 
 // Running max update with lazy rescale of the accumulator. The tile maximum
 // is a max3 tree over the lane's 32 scores (16 instructions).
-template <int D, bool ENT = false>
-__device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m, float& l, float& w,
-                                           float c) {
+template <int D>
+__device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D / 32], float& m, float& l, float c) {
   float t[12];
 #pragma unroll
   for (int i = 0; i < 10; ++i) {
@@ -49,8 +48,6 @@ __device__ __forceinline__ void update_max(const f32x16 (&s)[2], f32x16 (&o)[D /
   if (__builtin_amdgcn_ballot_w64(mx > m + kRescaleThreshold)) {
     const float mn = fmaxf(m, mx);
     const float alpha = fast_exp2(m - mn);
-    // w (entropy rows only): the sum of p (logit - max), moved to the new maximum
-    if constexpr (ENT) w = l > 0.f ? alpha * fmaf(m - mn, l, w) : 0.f;
     l *= alpha;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt) o[mt] *= alpha;
@@ -84,11 +81,10 @@ __device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const F
 // slice of the exponentials; sched_barrier keeps the steps apart so the
 // compiler does not regroup all MFMAs first. hook(ks) runs after step ks's
 // MFMAs are issued (the caller's tile copies go there).
-template <int D, bool ENT, bool PIN, typename Hook>
+template <int D, bool PIN, typename Hook>
 __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* kl, const FlashOffsets<D>& fo,
                                                   const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
-                                                  bf16x8 (&pb)[4], float& l, float& w, float c, float m,
-                                                  Hook&& hook) {
+                                                  bf16x8 (&pb)[4], float& l, float c, float m, Hook&& hook) {
   constexpr int KS = D / 16;
   constexpr int PER = 32 / KS;  // weights per step, even
   sn[0] = f32x16{};
@@ -113,10 +109,6 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
       const float p1 = fast_exp2(z1);
       pp[i >> 1] = bf16x2{static_cast<bf16>(p0), static_cast<bf16>(p1)};
       l = sum2(pp[i >> 1], l);
-      if constexpr (ENT) {
-        if (p0 > 0.f) w = fmaf(p0, z0, w);
-        if (p1 > 0.f) w = fmaf(p1, z1, w);
-      }
       // pin the weights to this step: without it the compiler sinks every
       // exponential of the tile below the last score MFMA in one of the two
       // unrolled steps, and that step loses its MFMA/VALU overlap (left out
@@ -135,9 +127,7 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
 }
 
 // exp2(s*c - m) as bf16 B operands for the four 16-key PV steps (last tile)
-template <bool ENT>
-__device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float& w, float c,
-                                      float m) {
+__device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], float& l, float c, float m) {
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     bf16x2 pp[4];
@@ -149,10 +139,6 @@ __device__ __forceinline__ void probs(const f32x16 (&s)[2], bf16x8 (&pb)[4], flo
       const float p1 = fast_exp2(z1);
       pp[e >> 1] = bf16x2{static_cast<bf16>(p0), static_cast<bf16>(p1)};
       l = sum2(pp[e >> 1], l);
-      if constexpr (ENT) {
-        if (p0 > 0.f) w = fmaf(p0, z0, w);
-        if (p1 > 0.f) w = fmaf(p1, z1, w);
-      }
     }
     pb[st] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
                                      __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
@@ -222,7 +208,6 @@ template <int D>
 struct FlashState {
   f32x16 o[D / 32];  // O^T accumulators
   float m, l;        // running max (scaled) and partial sum
-  float w;           // entropy rows only: partial sum of p (logit - max)
 };
 
 // Query tile qt (rows qt*qrows .. +qrows, qrows a multiple of 32 and at most
@@ -286,7 +271,6 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   for (int mt = 0; mt < D / 32; ++mt) st.o[mt] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
-  st.w = 0.f;
   wait_dma();
   __syncthreads();
 
@@ -313,7 +297,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
     if (!active && kc) td.dma(kdma, rk, (j + 2) * tile_bytes, wave);
     if (active) {
       if constexpr (KB) add_kbias(s, kbread, h, c);
-      update_max<D, ENT>(s, st.o, st.m, st.l, st.w, cs);
+      update_max<D>(s, st.o, st.m, st.l, cs);
       bf16x8 pb[4];
 #if MONARCH_PRIO == 2
       __builtin_amdgcn_s_setprio(1);
@@ -321,8 +305,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
       // the wave's copy instructions go one per score step (V's first, then
       // K's) instead of back to back before them: stage 1 at the frame shape
       // measured 1.7% faster
-      scores_with_probs<D, ENT, !ENT && !OUT_F32 && !DELTA && !KB && POLICY == 0>(sn, kread, fo, qf, s, pb, st.l, st.w, cs,
-                                                                            st.m,
+      scores_with_probs<D, !OUT_F32 && !DELTA && !KB && POLICY == 0>(sn, kread, fo, qf, s, pb, st.l, cs, st.m,
                                                             [&](int ks) {
         constexpr int IPW = TileDma<D, NW>::IPW;
         static_assert(2 * IPW <= D / 16, "one copy instruction per score step");
@@ -357,9 +340,9 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   f32x16 sl[2] = {odd ? sb[0] : sa[0], odd ? sb[1] : sa[1]};
   if constexpr (KB) add_kbias(sl, ((n - 1) & 1) ? kb1 : kb0, h, c);
   if (nv_last < FBN) mask_tail(sl, nv_last, h);
-  update_max<D, ENT>(sl, st.o, st.m, st.l, st.w, cs);
+  update_max<D>(sl, st.o, st.m, st.l, cs);
   bf16x8 pb[4];
-  probs<ENT>(sl, pb, st.l, st.w, cs, st.m);
+  probs(sl, pb, st.l, cs, st.m);
   pv64<D>(st.o, ((n - 1) & 1) ? v1 : v0, fo, pb, nv_last > 32 ? 4 : 2);
 
   const float lsum = halves_sum(st.l);  // both lane halves of a row are active together
@@ -370,8 +353,27 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   if (a.lse && h == 0 && row0 + r < Lq)
     a.lse[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = st.m + __builtin_amdgcn_logf(lsum);
   if constexpr (ENT) {
-    // entropy in bits: log2 of the denominator minus the mean of (logit - max)
-    const float w = halves_sum(st.w);
+    // Entropy in bits of the row's weights p_k = 2^(c s_k - m) / l: log2 l minus the
+    // weighted mean of (c s_k - m). The values of this pass are the keys (flash_supported),
+    // so sum_k p_k s_k = <q, sum_k p_k k_k> = <q, O_acc>: the weighted sum is
+    // c <q, O_acc> - m l, one dot product per row at the end instead of a term per score
+    // in the loop. q is read in the accumulator layout (register i of tile mt: channel
+    // 32 mt + 8 (i / 4) + 4 h + i % 4), 4 channels (8 bytes) at a time.
+    const uint32_t rowel = static_cast<uint32_t>(row0 + r) * static_cast<uint32_t>(rs * D);
+    float acc = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 qv = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rq, static_cast<int>((rowel + 32 * mt + 8 * g + 4 * h) * 2), 0, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t bits = (e & 1) ? (qv[e >> 1] & 0xffff0000u) : (qv[e >> 1] << 16);
+          acc = fmaf(st.o[mt][4 * g + e], __uint_as_float(bits), acc);
+        }
+      }
+    const float w = fmaf(c, halves_sum(acc), -st.m * lsum);
     if (h == 0 && row0 + r < Lq)
       a.ent[hd * (a.head_elems / D) + qbase + (row0 + r) * rs] = __builtin_amdgcn_logf(lsum) - w / lsum;
   }
@@ -843,7 +845,8 @@ hipError_t launch_group_d(const GroupedArgs& a, hipStream_t s) {
 
 bool flash_supported(const GroupedArgs& a) {
   return mfma_types_ok(a) && a.L > 128 && offsets_fit(a, FBN) &&
-         !(a.kbias && (a.ent || a.delta || a.o_type != kBF16)) && !(a.ent && (a.delta || a.o_type != kBF16));
+         !(a.kbias && (a.ent || a.delta || a.o_type != kBF16)) &&
+         !(a.ent && (a.delta || a.o_type != kBF16 || a.v != a.k));
 }
 
 hipError_t launch_flash(const GroupedArgs& a, hipStream_t s) {
