@@ -2,12 +2,17 @@
 //
 // This is the fp32 path (fp32 products keep the 1e-5 bound that reduced-
 // precision matrix cores would break) and the reference-shaped fallback for
-// shapes the MFMA kernels do not cover. One thread holds 64 of the D
-// channels of one query row (D/64 threads per row) with its output
-// accumulator in registers; keys and values are staged through LDS in chunks
-// of KC rows, converted to fp32. Softmax is online (running max and sum per
-// row, exp2 with the scale folded in), with one rescale of the accumulator per
-// chunk.
+// shapes the MFMA kernels do not cover. A query row is shared by D/16 lanes
+// of one wave, each holding 16 of its channels (query slice and output
+// accumulator in registers): a score is 16 FMAs per lane and a butterfly sum
+// over the row's lanes, and every lane then has the row's full softmax state.
+// Keys and values are staged through LDS in chunks of KC rows, row-major, so
+// a lane reads its 16 channels of a key as four 16-byte reads (the lanes of
+// one row read one contiguous row, the rows of a wave read the same one).
+// Softmax is online (running max and sum per row, exp2 with the scale folded
+// in), with one rescale of the accumulator per chunk. Sixteen channels per
+// lane keep the registers few and a workgroup at four waves even for short
+// problems, which are latency-bound.
 #include "internal.h"
 
 #include <math.h>
@@ -15,9 +20,8 @@
 namespace monarch {
 namespace {
 
-constexpr int KC = 32;          // keys per LDS chunk
-constexpr int PART = 64;        // channels per thread
-constexpr int PSTRIDE = PART + 1;
+constexpr int KC = 32;    // keys per LDS chunk
+constexpr int PART = 16;  // channels per lane
 
 __device__ __forceinline__ float load_elem(const void* base, int64_t idx, ElemType t) {
   if (t == kF32) return static_cast<const float*>(base)[idx];
@@ -31,12 +35,19 @@ __device__ __forceinline__ void store_elem(void* base, int64_t idx, float x, Ele
     static_cast<__bf16*>(base)[idx] = static_cast<__bf16>(x);
 }
 
+// sum of x over the SPLIT consecutive lanes of one row (SPLIT a power of two <= 8)
+template <int SPLIT>
+__device__ __forceinline__ float row_sum(float x) {
+#pragma unroll
+  for (int off = SPLIT / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, SPLIT);
+  return x;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_per_wg, int chunks) {
   constexpr int SPLIT = D / PART;
-  // [part][key][PSTRIDE]: the two halves of a row sit 32 banks apart
-  __shared__ float ks[SPLIT][KC][PSTRIDE];
-  __shared__ float vs[SPLIT][KC][PSTRIDE];
+  __shared__ __attribute__((aligned(16))) float ks[KC][D];
+  __shared__ __attribute__((aligned(16))) float vs[KC][D];
 
   const int64_t wg = blockIdx.x;
   const int chunk = static_cast<int>(wg % chunks);
@@ -76,8 +87,8 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
         kv = load_elem(a.k, g, a.qk_type);
         vv = load_elem(a.v, g, a.v_type);
       }
-      ks[e / PART][key][e % PART] = kv;
-      vs[e / PART][key][e % PART] = vv;
+      ks[key][e] = kv;
+      vs[key][e] = vv;
     }
     __syncthreads();
 
@@ -85,10 +96,17 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
     float cmax = -INFINITY;
 #pragma unroll
     for (int j = 0; j < KC; ++j) {
+      const float4* kr = reinterpret_cast<const float4*>(&ks[j][part * PART]);
       float s = 0.f;
 #pragma unroll
-      for (int e = 0; e < PART; ++e) s = fmaf(qr[e], ks[part][j][e], s);
-      if (SPLIT == 2) s += __shfl_xor(s, 1);
+      for (int c4 = 0; c4 < PART / 4; ++c4) {
+        const float4 k4 = kr[c4];
+        s = fmaf(qr[4 * c4 + 0], k4.x, s);
+        s = fmaf(qr[4 * c4 + 1], k4.y, s);
+        s = fmaf(qr[4 * c4 + 2], k4.z, s);
+        s = fmaf(qr[4 * c4 + 3], k4.w, s);
+      }
+      s = row_sum<SPLIT>(s);
       if (kb && j < nk) s += kb[static_cast<int64_t>(k0 + j) * a.row_stride];
       sc[j] = (j < nk) ? s : -INFINITY;
       cmax = fmaxf(cmax, sc[j]);
@@ -106,8 +124,15 @@ __global__ void __launch_bounds__(256) generic_kernel(GroupedArgs a, int rows_pe
       const float pj = exp2f(z);
       l += pj;
       if (pj > 0.f) wsum = fmaf(pj, z, wsum);
+      const float4* vr = reinterpret_cast<const float4*>(&vs[j][part * PART]);
 #pragma unroll
-      for (int e = 0; e < PART; ++e) acc[e] = fmaf(pj, vs[part][j][e], acc[e]);
+      for (int c4 = 0; c4 < PART / 4; ++c4) {
+        const float4 v4 = vr[c4];
+        acc[4 * c4 + 0] = fmaf(pj, v4.x, acc[4 * c4 + 0]);
+        acc[4 * c4 + 1] = fmaf(pj, v4.y, acc[4 * c4 + 1]);
+        acc[4 * c4 + 2] = fmaf(pj, v4.z, acc[4 * c4 + 2]);
+        acc[4 * c4 + 3] = fmaf(pj, v4.w, acc[4 * c4 + 3]);
+      }
     }
     m = m_new;
   }
