@@ -88,12 +88,14 @@ __device__ __forceinline__ void scores64(f32x16 (&s)[2], const char* kl, const F
 // slice of the exponentials; sched_barrier keeps the steps apart so the
 // compiler does not regroup all MFMAs first. hook(ks) runs after step ks's
 // MFMAs are issued (the caller's tile copies go there).
-template <int D, bool PIN, typename Hook>
+template <int D, bool PIN, typename Hook, int NP = 32>
 __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* kl, const FlashOffsets<D>& fo,
                                                   const bf16x8 (&qf)[D / 16], const f32x16 (&s)[2],
                                                   bf16x8 (&pb)[4], float& l, float c, float m, Hook&& hook) {
+  // NP: weights (of the lane's 32) computed here, the first NP; the rest in the value product
   constexpr int KS = D / 16;
-  constexpr int PER = 32 / KS;  // weights per step, even
+  constexpr int PER = NP / KS;  // weights per step, even
+  static_assert(PER % 2 == 0 && NP % 8 == 0, "whole weight pairs per step, whole PV steps");
   sn[0] = f32x16{};
   sn[1] = f32x16{};
   bf16x2 pp[16];
@@ -127,7 +129,7 @@ __device__ __forceinline__ void scores_with_probs(f32x16 (&sn)[2], const char* k
     a1 = n1;
   }
 #pragma unroll
-  for (int st = 0; st < 4; ++st)
+  for (int st = 0; st < NP / 8; ++st)
     pb[st] = __builtin_shufflevector(__builtin_shufflevector(pp[4 * st], pp[4 * st + 1], 0, 1, 2, 3),
                                      __builtin_shufflevector(pp[4 * st + 2], pp[4 * st + 3], 0, 1, 2, 3), 0, 1, 2,
                                      3, 4, 5, 6, 7);
@@ -179,9 +181,12 @@ __device__ __forceinline__ void pv64(f32x16 (&o)[D / 32], const char* vl, const 
 // taken on the side: each step's four MFMAs carry a max over 8 of the lane's
 // 32 scores (5 VALU instructions), so the max tree runs while the matrix core
 // works instead of in front of the next tile's exponentials.
-template <int D>
+// NP < 32: the weights NP..31 of the current tile (scores s) are computed here,
+// 8 per step in the first steps, each just before the PV step that takes them.
+template <int D, int NP = 32>
 __device__ __forceinline__ void pv64_max(f32x16 (&o)[D / 32], const char* vl, const FlashOffsets<D>& fo,
-                                         const bf16x8 (&pb)[4], const f32x16 (&sm)[2], float& mx) {
+                                         bf16x8 (&pb)[4], const f32x16 (&sm)[2], float& mx, const f32x16 (&s)[2],
+                                         float& l, float c, float m) {
   constexpr int MT = D / 32;
   bf16x8 v[MT];
 #pragma unroll
@@ -193,6 +198,20 @@ __device__ __forceinline__ void pv64_max(f32x16 (&o)[D / 32], const char* vl, co
     for (int mt = 0; mt < MT; ++mt) nv[mt] = (st + 1 < 4) ? v_operand<D>(vl, fo, mt, st + 1) : v[mt];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[mt] = mma(v[mt], pb[st], o[mt]);
+    if (NP / 8 + st < 4) {
+      // weights of PV step NP / 8 + st
+      const int ps = NP / 8 + st;
+      bf16x2 pp[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float z0 = fmaf(s[ps >> 1][8 * (ps & 1) + e], c, -m);
+        const float z1 = fmaf(s[ps >> 1][8 * (ps & 1) + e + 1], c, -m);
+        pp[e >> 1] = bf16x2{static_cast<bf16>(fast_exp2(z0)), static_cast<bf16>(fast_exp2(z1))};
+        l = sum2(pp[e >> 1], l);
+      }
+      pb[ps] = __builtin_shufflevector(__builtin_shufflevector(pp[0], pp[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pp[2], pp[3], 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
+    }
     const int t = st >> 1, b = 8 * (st & 1);
     const float q = max3(max3(sm[t][b], sm[t][b + 1], sm[t][b + 2]), max3(sm[t][b + 3], sm[t][b + 4], sm[t][b + 5]),
                          fmaxf(sm[t][b + 6], sm[t][b + 7]));
@@ -227,6 +246,13 @@ __device__ __forceinline__ void add_kbias(f32x16 (&s)[2], const float* kb, int h
       s[t][4 * g + 3] = fmaf(s[t][4 * g + 3], c, b.w);
     }
 }
+
+// Weights of a tile (of a lane's 32) computed beside the next tile's score
+// MFMAs; the other 16 are computed beside the first two value-product steps,
+// which balances the VALU work between the two MFMA phases (ABBA on one box,
+// all 32 beside the scores -> 16: frame stage 1 -0.6%, row stage 2 -1.5%,
+// dense -0.3%; bitwise the same results)
+constexpr int kScoreWeights = 16;
 
 // Wave priority while issuing MFMA-heavy phases (MONARCH_PRIO): 0 = never
 // raised; 1 = raised for the value product; 2 = raised for scores + values
@@ -346,13 +372,15 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
       // the wave's copy instructions go one per score step (V's first, then
       // K's) instead of back to back before them: stage 1 at the frame shape
       // measured 1.7% faster
-      scores_with_probs<D, !OUT_F32 && !DELTA && !KB && POLICY == 0>(sn, kread, fo, qf, s, pb, st.l, cs, st.m,
-                                                            [&](int ks) {
+      auto copy_hook = [&](int ks) {
         constexpr int IPW = TileDma<D, NW>::IPW;
         static_assert(2 * IPW <= D / 16, "one copy instruction per score step");
         if (ks < IPW) td.dma1(vdma, rv, (j + 1) * tile_bytes, wave, ks);
         if (ks >= IPW && ks < 2 * IPW && kc) td.dma1(kdma, rk, (j + 2) * tile_bytes, wave, ks - IPW);
-      });
+      };
+      scores_with_probs<D, !OUT_F32 && !DELTA && !KB && POLICY == 0, decltype(copy_hook)&, EM ? kScoreWeights : 32>(
+          sn, kread, fo, qf, s, pb, st.l, cs, st.m, copy_hook);
+
 #if MONARCH_PRIO == 1
       __builtin_amdgcn_s_setprio(1);
 #endif
@@ -360,7 +388,7 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
         // the last tile's keys past the end are masked before its maximum is taken
         if (j + 2 == n && nv_last < FBN) mask_tail(sn, nv_last, h);
         float mx;
-        pv64_max<D>(st.o, vread, fo, pb, sn, mx);
+        pv64_max<D, kScoreWeights>(st.o, vread, fo, pb, sn, mx, s, st.l, cs, st.m);
 #if MONARCH_PRIO
         __builtin_amdgcn_s_setprio(0);
 #endif
