@@ -124,6 +124,8 @@ def trace_summary(path: str, config: str, kernel: str) -> None:
     # the MFMA flash kernel takes the stage whose problems exceed 128 rows (stage 1: b rows,
     # stage 2: m_tau rows); its algorithmic FLOP per launch are that stage's
     stage, L = ("stage-1", b) if b > 128 else ("stage-2", m)
+    if "fused" in kernel:  # the one-launch forward does both stages
+        stage, L = "fused", b + m
     flops1 = 4 * c["batch"] * c["heads"] * N * L * c["d"]
     rows = sorted(csv.DictReader(open(path)), key=lambda r: int(r["Start_Timestamp"]))
     by = {}
