@@ -143,7 +143,7 @@ monarch_status monarch_attn_plan(monarch_plan** out, int32_t batch, int32_t head
 void monarch_attn_destroy(monarch_plan* plan);
 
 /* Bytes of device workspace monarch_attn_forward needs (0 when b = 1 or m_tau = 1): Y, plus a
- * control block of a few hundred bytes when the plan is fused. */
+ * control block of 128 bytes plus 128 per (batch x head, tile) when the plan is fused. */
 size_t monarch_attn_workspace_size(const monarch_plan* plan);
 
 /* Copy the plan's derived sizes into *info. */

@@ -708,30 +708,21 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
 }
 
 // ---------------------------------------------------------------- fused
-// Both stages in one persistent launch. Work items are stage-1 query tiles
+// Both stages in one launch (fused_grid_kernel below): stage-1 query tiles
 // (as flash_kernel) and stage-2 chunks of kFusedGroups groups (m_tau <= 32
-// rows each). Each XCD owns a contiguous share of both lists and hands its
-// items out in order through its own ticket counter, stage-1 tiles first, so
-// the query tiles of one problem stay on one XCD (shared L2) and a workgroup
-// that draws a stage-2 chunk knows that every stage-1 tile of its XCD has
-// already been drawn by a running workgroup.
+// rows each).
 //
 // Y crosses XCDs, whose L2 caches are not coherent with one another. It is
 // written with device-scope stores (written through the L2) and read with
 // device-scope loads, so no L2 writeback or invalidation is needed (each
-// costs a whole-L2 operation). A stage-1 tile counts itself in ready[head,
-// tile] once its Y stores have completed; a stage-2 chunk waits until its
-// (head, tile) counter reaches m_tau * qtiles before loading Y. The wait
-// always ends: every tile it counts has been drawn by a workgroup that is
-// running or done, and stage-1 tiles never wait. A spin bound (far above any
-// legitimate wait) sets an error word instead of hanging if that were ever
-// violated (e.g. an XCD with no workgroups).
+// costs a whole-L2 operation).
 //
-// Control block (ints): [0, 8) tickets per XCD, [8] error, [16, ...) ready.
+// Control block (ints): [0, 16) the per-XCD claim words (8 x 64 bits),
+// [16] error, [32, ...) ready counters, one per (head, tile), 32 ints apart.
 constexpr int kFusedXcds = 8;
 constexpr int kFusedGroups = 16;  // stage-2 groups per work item, 4 per wave
-constexpr int kCtlError = 8;
-constexpr int kCtlReady = 16;
+constexpr int kCtlError = 2 * kFusedXcds;
+constexpr int kCtlReady = 2 * kFusedXcds + 16;
 
 __global__ void __launch_bounds__(256) fused_reset(int* ctl, int n) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) ctl[i] = 0;
@@ -800,80 +791,110 @@ __device__ __forceinline__ void group_wave(const GroupedArgs& a, int hd, int p, 
   store_out<D, false>(ro, lane & 31, rs, o, inv, lane);
 }
 
+// Both stages in one launch of n1 + n2 workgroups: n1
+// stage-1 query tiles, then n2 stage-2 chunks in head order.
+//
+// Stage-1 tiles are claimed, not indexed by workgroup id: the blocks (problems
+// of all heads, in head order) are dealt to the XCDs round-robin, block B to
+// list B mod nxcd, each list holding its blocks' query tiles in order. A
+// workgroup claims the next tile from the front of its own XCD's list; when
+// that list is used up it claims from the back of another list. So all query
+// tiles of a block run on one XCD (shared L2) except for a few at the end,
+// and the XCDs work through the blocks, hence the heads, together: the first
+// heads' Y is complete while the last tiles still run, and their stage-2
+// chunks (dispatched once every stage-1 workgroup has been) fill the
+// workgroup slots the last tiles leave free. A list's front and back counts
+// share one 64-bit word, so every claim sees all earlier ones: a claim is
+// valid iff fewer than the list's length were taken before it, and every
+// stage-1 workgroup finds a tile (there are as many tiles as workgroups).
+//
+// Each tile counts itself in ready[head, tile] (one 128-byte line per
+// counter) once its written-through Y stores have completed; a stage-2 chunk
+// waits for its count and reads Y with device-scope loads. Workgroups start
+// in index order on each XCD, so every stage-1 tile has started before any
+// stage-2 chunk of its XCD and never waits: the wait ends (the spin bound and
+// the error word remain as a guard).
+constexpr int kCtlClaims = 0;  // nxcd 64-bit words: front count (low half), back count (high half)
+constexpr int kReadyStride = 32;
+
+__device__ __forceinline__ bool claim_tile(int* ctl, int list, bool back, int nb, int nxcd, int qtiles, int& blk,
+                                           int& qt) {
+  const int nblk = (nb - list + nxcd - 1) / nxcd;  // blocks list, list + nxcd, ...
+  const int len = nblk * qtiles;
+  unsigned long long* w = reinterpret_cast<unsigned long long*>(ctl + kCtlClaims) + list;
+  const unsigned long long old =
+      __hip_atomic_fetch_add(w, back ? (1ull << 32) : 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int front = static_cast<int>(old & 0xffffffffu), taken_back = static_cast<int>(old >> 32);
+  if (front + taken_back >= len) return false;
+  const int j = back ? len - 1 - taken_back : front;
+  blk = list + nxcd * (j / qtiles);
+  qt = j % qtiles;
+  return true;
+}
+
 template <int D>
-__global__ void __launch_bounds__(FNT, 2) fused_kernel(FusedArgs f, int qtiles, int nchunks, int nxcd) {
+__global__ void __launch_bounds__(FNT, 2) fused_grid_kernel(FusedArgs f, int qtiles, int nchunks, int n1, int nxcd) {
   using T = SwTile<D>;
   __shared__ __attribute__((aligned(1024))) char k0[T::bytes];
   __shared__ __attribute__((aligned(1024))) char k1[T::bytes];
   __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
   __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
-  __shared__ int ticket;
+  __shared__ int item[2];
   __shared__ int timed_out;
-
   const int tid = threadIdx.x;
-  // hardware XCD of this workgroup (HW_REG_XCC_ID, bits 3:0)
-  const int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % nxcd;
-  const int64_t n1 = static_cast<int64_t>(qtiles) * f.s1.problems * f.s1.heads;
-  const int64_t n2 = static_cast<int64_t>(nchunks) * f.tiles * f.s2.heads;
-  const int b1 = static_cast<int>(n1 * xcd / nxcd), c1 = static_cast<int>(n1 * (xcd + 1) / nxcd) - b1;
-  const int b2 = static_cast<int>(n2 * xcd / nxcd), c2 = static_cast<int>(n2 * (xcd + 1) / nxcd) - b2;
-  const int target = f.m_tau * qtiles;
   int* ready = f.ctl + kCtlReady;
-  int acquired = -1;
-
-  for (;;) {
-    __syncthreads();  // LDS slots and `ticket` are free again
-    if (tid == 0) ticket = atomicAdd(f.ctl + xcd, 1);
+  if (static_cast<int>(blockIdx.x) < n1) {
+    if (tid == 0) {
+      // hardware XCD of this workgroup (HW_REG_XCC_ID, bits 3:0)
+      const int xcd = static_cast<int>(__builtin_amdgcn_s_getreg((3 << 11) | 20)) % nxcd;
+      const int nb = f.s1.problems * f.s1.heads;
+      int blk = -1, qt = 0;
+      if (!claim_tile(f.ctl, xcd, false, nb, nxcd, qtiles, blk, qt))
+        for (int d = 1; d < nxcd && blk < 0; ++d)
+          if (!claim_tile(f.ctl, (xcd + d) % nxcd, true, nb, nxcd, qtiles, blk, qt)) blk = -1;
+      item[0] = blk;
+      item[1] = qt;
+    }
     __syncthreads();
-    const int t = ticket;
-    if (t >= c1 + c2) break;
-    // the thread index passed on is made opaque, so the per-lane offsets of
-    // each item are computed inside it instead of being hoisted out of this
-    // loop and kept live (in spilled registers) across both kinds of item
-    int otid = tid;
-    asm volatile("" : "+v"(otid));
-    if (t < c1) {
-      const int id = b1 + t;
-      const int qt = id % qtiles, rest = id / qtiles;
-      const int p = rest % f.s1.problems, hd = rest / f.s1.problems;
-      flash_tile<D, false, kPolicyDevice>(f.s1, hd, p, qt, FBM, k0, k1, v0, v1, otid);
-      wait_dma();  // this wave's written-through Y stores have completed
-      __syncthreads();
-      if (tid == 0)
-        __hip_atomic_fetch_add(ready + hd * f.tiles + p / f.m_tau, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const int id = b2 + (t - c1);
-      const int chunk = id % nchunks, rest = id / nchunks;
-      const int u = rest % f.tiles, hd = rest / f.tiles;
-      const int key = hd * f.tiles + u;
-      if (key != acquired) {
-        if (tid == 0) {
-          int spins = 0, late = 0;
-          while (__hip_atomic_load(ready + key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(8);
-            if (++spins > (1 << 20)) {
-              __hip_atomic_store(f.ctl + kCtlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              late = 1;
-              break;
-            }
-          }
-          timed_out = late;
-        }
-        __syncthreads();  // Y is read below with device-coherent loads only
-        acquired = key;
-      }
-      const bool poison = timed_out != 0;
-      const int w = otid >> 6;
-      char* const lds_wave = w == 0 ? k0 : w == 1 ? k1 : w == 2 ? v0 : v1;
-      const FlashOffsets<D> fo(w, otid & 63, f.s2.row_stride);
-      const int j0 = chunk * kFusedGroups;
-#pragma unroll 1
-      for (int g = w; g < kFusedGroups; g += 4) {
-        const int j = j0 + g;
-        if (j >= f.b) break;
-        group_wave<D>(f.s2, hd, u * f.b + j, lds_wave, lds_wave + 32 * 2 * D, fo, otid & 63, poison);
+    const int blk = item[0], qt = item[1];
+    if (blk < 0) return;  // cannot happen (as many tiles as workgroups); no counter waits on it
+    const int p = blk % f.s1.problems, hd = blk / f.s1.problems;
+    flash_tile<D, false, kPolicyDevice>(f.s1, hd, p, qt, FBM, k0, k1, v0, v1, tid);
+    wait_dma();  // this wave's written-through Y stores have completed
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(ready + kReadyStride * (hd * f.tiles + p / f.m_tau), 1, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  const int id = static_cast<int>(blockIdx.x) - n1;
+  const int chunk = id % nchunks, rest = id / nchunks;
+  const int u = rest % f.tiles, hd = rest / f.tiles;
+  const int key = hd * f.tiles + u;
+  const int target = f.m_tau * qtiles;
+  if (tid == 0) {
+    int spins = 0, late = 0;
+    while (__hip_atomic_load(ready + kReadyStride * key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+      __builtin_amdgcn_s_sleep(32);
+      if (++spins > (1 << 18)) {
+        __hip_atomic_store(f.ctl + kCtlError, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        late = 1;
+        break;
       }
     }
+    timed_out = late;
+  }
+  __syncthreads();  // Y is read below with device-coherent loads only
+  const bool poison = timed_out != 0;
+  const int w = tid >> 6;
+  char* const lds_wave = w == 0 ? k0 : w == 1 ? k1 : w == 2 ? v0 : v1;
+  const FlashOffsets<D> fo(w, tid & 63, f.s2.row_stride);
+  const int j0 = chunk * kFusedGroups;
+#pragma unroll 1
+  for (int g = w; g < kFusedGroups; g += 4) {
+    const int j = j0 + g;
+    if (j >= f.b) break;
+    group_wave<D>(f.s2, hd, u * f.b + j, lds_wave, lds_wave + 32 * 2 * D, fo, tid & 63, poison);
   }
 }
 
@@ -953,7 +974,7 @@ bool fused_supported(const GroupedArgs& s1, const GroupedArgs& s2) {
          s2.Lq == s2.L;
 }
 
-int64_t fused_ctl_ints(int64_t heads, int64_t tiles) { return kCtlReady + heads * tiles; }
+int64_t fused_ctl_ints(int64_t heads, int64_t tiles) { return kCtlReady + 32 * heads * tiles; }
 int64_t fused_ctl_error_index() { return kCtlError; }
 
 hipError_t launch_fused(const FusedArgs& f, hipStream_t s) {
@@ -970,11 +991,16 @@ hipError_t launch_fused(const FusedArgs& f, hipStream_t s) {
   hipLaunchKernelGGL(fused_reset, dim3(1), dim3(256), 0, s, f.ctl, static_cast<int>(nctl));
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = 2 * (cus > 0 ? cus : 1);  // two resident workgroups per CU
+  const int64_t n1 = static_cast<int64_t>(qtiles) * f.s1.problems * f.s1.heads;
+  const int64_t n2 = static_cast<int64_t>(nchunks) * f.tiles * f.s2.heads;
+  if (n1 + n2 > 0x7fffffff) return hipErrorInvalidConfiguration;
+  const unsigned grid = static_cast<unsigned>(n1 + n2);
   if (f.s1.D == 128)
-    hipLaunchKernelGGL((fused_kernel<128>), dim3(grid), dim3(FNT), 0, s, f, qtiles, nchunks, nxcd);
+    hipLaunchKernelGGL((fused_grid_kernel<128>), dim3(grid), dim3(FNT), 0, s, f, qtiles, nchunks, static_cast<int>(n1),
+                       nxcd);
   else
-    hipLaunchKernelGGL((fused_kernel<64>), dim3(grid), dim3(FNT), 0, s, f, qtiles, nchunks, nxcd);
+    hipLaunchKernelGGL((fused_grid_kernel<64>), dim3(grid), dim3(FNT), 0, s, f, qtiles, nchunks, static_cast<int>(n1),
+                       nxcd);
   return hipGetLastError();
 }
 

@@ -220,12 +220,12 @@ def test_fused_plan_applies_to_frame_and_tiled_bf16():
     info, ws = _info(heads=12, grid=(21, 30, 52), flags=_lib.FLAG_FUSED)
     assert info.fused == 1
     y = 12 * 32760 * 128 * 2
-    assert ws == (y + 255) // 256 * 256 + (16 + 12 * 1) * 4
+    assert ws == (y + 255) // 256 * 256 + (32 + 32 * 12 * 1) * 4
     # the separate stages keep their own kernels (stage1/stage2 entry points)
     assert L.monarch_attn_kernel_name(info.stage1_kernel) == b"flash_mfma_bf16"
     info, ws = _info(heads=12, grid=(21, 30, 52), tile=4680, flags=_lib.FLAG_FUSED)
     assert info.fused == 1 and info.tiles == 7
-    assert ws == (y + 255) // 256 * 256 + (16 + 12 * 7) * 4
+    assert ws == (y + 255) // 256 * 256 + (32 + 32 * 12 * 7) * 4
     assert L.monarch_attn_kernel_name(5) == b"fused_mfma_bf16"
 
 
@@ -397,5 +397,5 @@ def test_refine_unsupported_entry_points():
 def test_fused_error_offset():
     info, ws = _info(heads=12, grid=(21, 30, 52), flags=_lib.FLAG_FUSED)
     y = 12 * 32760 * 128 * 2
-    assert info.fused == 1 and info.fused_error_offset == (y + 255) // 256 * 256 + 8 * 4
+    assert info.fused == 1 and info.fused_error_offset == (y + 255) // 256 * 256 + 16 * 4
     assert info.fused_error_offset + 4 <= ws
