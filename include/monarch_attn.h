@@ -79,12 +79,13 @@ typedef enum monarch_align {
 #define MONARCH_FLAG_Y_FP32 (1u << 0)          /* keep Y in fp32 for bf16 inputs (default: bf16) */
 #define MONARCH_FLAG_ALLOW_UNALIGNED (1u << 1) /* accept a custom b that cuts a grid axis */
 #define MONARCH_FLAG_GENERIC (1u << 2)         /* force the plain VALU kernels (diagnostics) */
-/* One launch for both stages, run as a persistent launch (a design choice of this library; the
- * pages describe no fused two-stage kernel): stage-2 groups start as soon as the stage-1 blocks
- * of their head and tile are done, filling the end of stage 1 instead of waiting for all of it.
- * Used only where it applies (bf16, Y bf16, b > 128, 2 <= m_tau <= 32: the frame and tiled
- * alignments); elsewhere the flag is ignored and monarch_plan_info.fused reports 0. It adds a
- * small control block to the workspace. */
+/* One launch for both stages (a design choice of this library; the pages describe no fused
+ * two-stage kernel): the stage-1 query tiles, then the stage-2 group chunks of the same grid,
+ * each chunk starting once the stage-1 blocks of its head and tile are done. Same result as the
+ * two launches; on MI355X it measures slower than them. Used only where it applies (bf16, Y
+ * bf16, b > 128, 2 <= m_tau <= 32: the frame and tiled alignments); elsewhere the flag is
+ * ignored and monarch_plan_info.fused reports 0. It adds a control block to the workspace
+ * (monarch_attn_workspace_size). */
 #define MONARCH_FLAG_FUSED (1u << 3)
 /* One refinement step of the Monarch factors. The pages say MonarchAttention fits its factors by
  * iterative refinement (about ten steps) and that MonarchRT needs a single step after finetuning
