@@ -538,16 +538,20 @@ __global__ void __launch_bounds__(64 * kFlashWaves, 2) flash_kernel(GroupedArgs 
   __shared__ __attribute__((aligned(1024))) char v0[T::bytes];
   __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
   const int id = xcd_order(blockIdx.x, nwg);
-  const int qt = id % qtiles;
+  // the workgroup's tile, problem and head are uniform: readfirstlane keeps them and the
+  // addresses derived from them in scalar registers (the integer divisions run on the vector
+  // unit, and vector copies of these values were spilled across the loop)
+  const int qt = __builtin_amdgcn_readfirstlane(id % qtiles);
   const int rest = id / qtiles;
+  const int p = __builtin_amdgcn_readfirstlane(rest % a.problems);
+  const int hd = __builtin_amdgcn_readfirstlane(rest / a.problems);
   if constexpr (KB) {
     __shared__ __attribute__((aligned(256))) float kb0[FBN];
     __shared__ __attribute__((aligned(256))) float kb1[FBN];
-    flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT, true>(a, rest / a.problems, rest % a.problems, qt, qrows, k0,
-                                                             k1, v0, v1, threadIdx.x, kb0, kb1);
+    flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT, true>(a, hd, p, qt, qrows, k0, k1, v0, v1, threadIdx.x, kb0,
+                                                             kb1);
   } else {
-    flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT>(a, rest / a.problems, rest % a.problems, qt, qrows, k0, k1,
-                                                       v0, v1, threadIdx.x);
+    flash_tile<D, OUT_F32, 0, kFlashWaves, DELTA, ENT>(a, hd, p, qt, qrows, k0, k1, v0, v1, threadIdx.x);
   }
 }
 
