@@ -576,13 +576,18 @@ struct GroupCfg {
   static constexpr int MINW = 3 * tile <= 80 * 1024 ? 2 : 1;
 };
 
-template <int D, int QT, bool OUT_F32>
-__global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)) group_kernel(GroupedArgs a) {
+// SR = 0: each tile holds 32 QT rows. SR = 24 (one wave, problems of at most
+// 24 rows): the three tiles hold 24 rows each and sit back to back, followed
+// by 8 zero rows, so the MFMAs' 32-row reads of a tile run into the next
+// tile's first rows (finite values: keys past the end are masked, query rows
+// past the end are not stored) and, for the values, into the zero rows (keys
+// past the end have weight 0). The smaller footprint (20 KB instead of 24 KB
+// at d = 128) lets eight workgroups share a CU instead of six.
+template <int D, int QT, bool OUT_F32, int SR>
+__device__ __forceinline__ void group_body(const GroupedArgs& a, char* ql, char* kl, char* vl) {
   using G = GroupCfg<D, QT>;
-  __shared__ __attribute__((aligned(1024))) char ql[G::tile];
-  __shared__ __attribute__((aligned(1024))) char kl[G::tile];
-  __shared__ __attribute__((aligned(1024))) char vl[G::tile];
-
+  static_assert(SR == 0 || QT == 1, "short tiles: one wave");
+  constexpr int IPW = (SR ? SR : 32) / G::RPI;  // DMA instructions per tile of this wave
   const int p = blockIdx.x % a.problems;
   const int hd = blockIdx.x / a.problems;
   const int64_t hoff = static_cast<int64_t>(hd) * a.head_elems;
@@ -598,9 +603,10 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
                                OUT_F32 ? 4 : 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
 
-  // wave w copies rows 32w .. 32w+31 of Q, K and V (rows past L read as zero)
+  // wave w copies rows 32w .. 32w+31 of Q, K and V (rows past L read as zero;
+  // short tiles: rows 0 .. SR-1)
 #pragma unroll
-  for (int i = 0; i < G::IPW; ++i) {
+  for (int i = 0; i < IPW; ++i) {
     const int row = 32 * wave + G::RPI * i + lane / G::CPR;
     const int c = (lane % G::CPR) ^ swz<D>(row);
     const uint32_t goff = static_cast<uint32_t>((row * rs * D + c * 8) * 2);
@@ -709,6 +715,29 @@ __global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)
       __builtin_amdgcn_raw_buffer_store_b128(v, ro, static_cast<int>((row * rs * D + chk * 8) * 2), 0, 0);
     }
   }
+}
+
+template <int D, int QT, bool OUT_F32>
+__global__ void __launch_bounds__((GroupCfg<D, QT>::NT), (GroupCfg<D, QT>::MINW)) group_kernel(GroupedArgs a) {
+  using G = GroupCfg<D, QT>;
+  __shared__ __attribute__((aligned(1024))) char ql[G::tile];
+  __shared__ __attribute__((aligned(1024))) char kl[G::tile];
+  __shared__ __attribute__((aligned(1024))) char vl[G::tile];
+  group_body<D, QT, OUT_F32, 0>(a, ql, kl, vl);
+}
+
+constexpr int kShortRows = 24;
+
+template <int D, bool OUT_F32>
+__global__ void __launch_bounds__(64, 2) group_short_kernel(GroupedArgs a) {
+  constexpr int ROWB = D * 2, TB = kShortRows * ROWB, PADB = 8 * ROWB;
+  __shared__ __attribute__((aligned(1024))) char lds[3 * TB + PADB];
+  // the 8 rows after the value tile read as zero
+  const int lane = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < PADB / 1024; ++i)
+    *reinterpret_cast<u32x4*>(lds + 3 * TB + 1024 * i + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+  group_body<D, 1, OUT_F32, kShortRows>(a, lds, lds + TB, lds + 2 * TB);
 }
 
 // ---------------------------------------------------------------- fused
@@ -939,6 +968,12 @@ hipError_t launch_group_t(const GroupedArgs& a, hipStream_t s) {
 
 template <int D, bool F32>
 hipError_t launch_group_d(const GroupedArgs& a, hipStream_t s) {
+  if (a.L <= kShortRows) {
+    const int64_t nwg = static_cast<int64_t>(a.problems) * a.heads;
+    if (nwg <= 0 || nwg > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((group_short_kernel<D, F32>), dim3(static_cast<unsigned>(nwg)), dim3(64), 0, s, a);
+    return hipGetLastError();
+  }
   switch ((a.L + 31) / 32) {
     case 1: return launch_group_t<D, 1, F32>(a, s);
     case 2: return launch_group_t<D, 2, F32>(a, s);
