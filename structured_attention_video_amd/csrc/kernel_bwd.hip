@@ -96,8 +96,11 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dq_kernel(BwdArgs b, int qtiles, i
   __shared__ __attribute__((aligned(1024))) char v1[T::bytes];
   const GroupedArgs& a = b.g;
   const int id = xcd_order(blockIdx.x, nwg);
-  const int qt = id % qtiles, rest = id / qtiles;
-  const int p = rest % a.problems, hd = rest / a.problems;
+  // uniform per workgroup: readfirstlane keeps the decode and the addresses derived from it
+  // in scalar registers
+  const int qt = __builtin_amdgcn_readfirstlane(id % qtiles), rest = id / qtiles;
+  const int p = __builtin_amdgcn_readfirstlane(rest % a.problems);
+  const int hd = __builtin_amdgcn_readfirstlane(rest / a.problems);
   const int64_t ntok = a.head_elems / D;
   const int64_t hoff = hd * a.head_elems;
   const int64_t base = problem_base(a, p);
@@ -111,7 +114,8 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dq_kernel(BwdArgs b, int qtiles, i
   const auto ro = problem_rsrc(static_cast<const char*>(b.dq) + hoff * (f32 ? 4 : 2), base, rs, L, D, f32 ? 4 : 2);
   const auto ra = problem_rsrc(b.dq_in ? b.dq_in + hoff : b.delta, base, rs, L, D, 4);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses stay scalar
   const int row0 = qt * FBM + wave * 32;
   const int r = row0 + (lane & 31);
   const int n = (L + FBN - 1) / FBN;
@@ -212,8 +216,10 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   __shared__ __attribute__((aligned(16))) float st_del[2][FBN];
   const GroupedArgs& a = b.g;
   const int id = xcd_order(blockIdx.x, nwg);
-  const int kt = id % ktiles, rest = id / ktiles;
-  const int p = rest % a.problems, hd = rest / a.problems;
+  // uniform per workgroup (as in bwd_dq_kernel)
+  const int kt = __builtin_amdgcn_readfirstlane(id % ktiles), rest = id / ktiles;
+  const int p = __builtin_amdgcn_readfirstlane(rest % a.problems);
+  const int hd = __builtin_amdgcn_readfirstlane(rest / a.problems);
   const int64_t ntok = a.head_elems / D;
   const int64_t hoff = hd * a.head_elems;
   const int64_t base = problem_base(a, p);
@@ -227,7 +233,8 @@ __global__ void __launch_bounds__(FNT, 2) bwd_dkdv_kernel(BwdArgs b, int ktiles,
   const auto rdk = problem_rsrc(static_cast<const char*>(b.dk) + hoff * (kf32 ? 4 : 2), base, rs, L, D, kf32 ? 4 : 2);
   const auto ra = problem_rsrc(b.dk_in ? b.dk_in + hoff : b.delta, base, rs, L, D, 4);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: copy addresses stay scalar
   const int key0 = kt * FBM + wave * 32;
   const int n = (L + FBN - 1) / FBN;
   const float c = a.scale_log2;
