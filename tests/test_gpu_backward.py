@@ -103,6 +103,19 @@ def test_backward_full_size(name, heads):
         assert np.array_equal(x, to_np(y))
 
 
+@pytest.mark.parametrize("align", ["frame", "row"])
+def test_backward_full_grid_head_dim_64(align):
+    # the d = 64 backward kernels at full problem length (tiled kernels over 1560-row blocks
+    # and 630-row groups, the one-pass kernels for 21-row groups and 52-row blocks), one head
+    grid = (21, 30, 52)
+    q, k, v = datagen.qkv(1, 1, grid, 64, (4010, 4011, 4012), dtype=BF16)
+    g = datagen.qkv(1, 1, grid, 64, (4013, 4014, 4015), dtype=BF16)[0]
+    got, _, _ = grads(q, k, v, g, grid, align, 0)
+    want = oracle.monarch_backward(q, k, v, g, oracle.block_size(grid, align), None)
+    for nm, x, y in zip(("dQ", "dK", "dV"), got, want):
+        check(x, y, f"d=64 {align} {nm}")
+
+
 SAVED = [SMALL[i] for i in (0, 1, 2, 5, 6, 8, 9, 12)] + [((21, 30, 52), 128, "frame", 0, 0)]
 
 

@@ -162,6 +162,18 @@ def test_full_size_workloads(name):
     assert_close(to_np(got), want, BF16, name)
 
 
+@pytest.mark.parametrize("align,tile", [("frame", 0), ("row", 0), ("frame", 4680)])
+def test_full_grid_head_dim_64(align, tile):
+    """The 21x30x52 grid at d = 64, four heads, every element: the d = 64 kernels at full
+    problem length (flash over 1560-row blocks and 630-row groups, the short-tile group
+    kernel for the 21-row groups, the tiny kernel for tiles of three blocks)."""
+    grid = (21, 30, 52)
+    q, k, v = datagen.qkv(1, 4, grid, 64, (4000, 4001, 4002))
+    got = run(q, k, v, grid, align, tile)
+    b = oracle.block_size(grid, align)
+    assert_close(to_np(got), ref(q, k, v, b, tile), BF16, f"d=64 {align} t{tile}")
+
+
 def test_long_video_all_heads():
     """The long workload (81 frames, N = 126360) on all 12 heads, every element."""
     c = datagen.CONFIGS["long_bf16"]
