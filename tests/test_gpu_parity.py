@@ -174,6 +174,17 @@ def test_full_grid_head_dim_64(align, tile):
     assert_close(to_np(got), ref(q, k, v, b, tile), BF16, f"d=64 {align} t{tile}")
 
 
+@pytest.mark.parametrize("align", ["frame", "row"])
+def test_full_grid_fp32(align):
+    """fp32 on the 21x30x52 grid, one head, every element, to the fp32 bound: the generic
+    kernel over 1560-key blocks (49 key chunks) and 630-row groups."""
+    grid = (21, 30, 52)
+    q, k, v = datagen.qkv(1, 1, grid, 128, (4020, 4021, 4022), dtype=F32)
+    got = run(q, k, v, grid, align)
+    b = oracle.block_size(grid, align)
+    assert_close(to_np(got), ref(q, k, v, b), F32, f"fp32 {align}")
+
+
 def test_long_video_all_heads():
     """The long workload (81 frames, N = 126360) on all 12 heads, every element."""
     c = datagen.CONFIGS["long_bf16"]
