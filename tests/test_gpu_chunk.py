@@ -50,6 +50,23 @@ def test_chunks_match_oracle(grid, d, dtype, align, cf):
         assert_close(o[:, :, t0 * H * W:t1 * H * W], want, dtype, f"chunk {t0}-{t1}")
 
 
+@pytest.mark.parametrize("align", ["frame", "row"])
+def test_full_size_chunks_match_oracle(align):
+    # the 21x30x52 grid as generated frame by frame: 18 frames, then the last 3 against the
+    # cached Y of the first 18 (the bench's chunk), two heads, every element of both chunks
+    name = "frame_bf16"
+    c = datagen.CONFIGS[name]
+    T, H, W = c["grid"]
+    q, k, v = datagen.config_inputs(name, heads=2)
+    plan = MonarchPlan(1, 2, 128, c["grid"], align=align)
+    b = plan.info["b"]
+    bounds = [(0, 18), (18, 21)]
+    o = to_np(chunks(plan, *(x.to(DEV) for x in (q, k, v)), bounds))
+    for t0, t1 in bounds:
+        want = oracle.monarch_chunk_forward(q, k, v, b, H * W, t0, t1)
+        assert_close(o[:, :, t0 * H * W:t1 * H * W], want, BF16, f"{align} chunk {t0}-{t1}")
+
+
 def test_whole_video_chunk_equals_forward_and_future_is_ignored():
     name = "frame_bf16"
     c = datagen.CONFIGS[name]

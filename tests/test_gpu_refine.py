@@ -100,6 +100,15 @@ def test_refine_full_size(name):
     assert_close(to_np(got[0, heads]), want, BF16, f"refine {name} heads {heads}")
 
 
+def test_refine_long_one_head():
+    # the long workload (81 frames, m = 81: stage 2 in the group kernel with key biases), head 0
+    c = datagen.CONFIGS["long_bf16"]
+    q, k, v = datagen.config_inputs("long_bf16", heads=1)
+    got = run(q, k, v, c["grid"], "frame")
+    want = oracle.monarch_refine_forward(q[0], k[0], v[0], oracle.block_size(c["grid"], "frame"), None)
+    assert_close(to_np(got[0]), want, BF16, "refine long head 0")
+
+
 def test_refine_separable_full_size_matches_dense():
     """Aligned blocks keep separable logits exactly (explainer section 2.A), so the refined
     factors give dense attention at the 21x30x52 grid; compared with the library's dense kernel
