@@ -145,13 +145,6 @@ struct TileDma {
 // wait for this wave's outstanding global -> LDS copies
 __device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
-// wait until at most N of this wave's vector memory loads are outstanding (N < 16)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 __device__ __forceinline__ void mask_tail(f32x16 (&s)[2], int nvalid, int h) {
 #pragma unroll
   for (int t = 0; t < 2; ++t)

@@ -318,27 +318,21 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   const uint32_t kb_lane = static_cast<uint32_t>(lane * rs * 4);
   const uint32_t kb_tile = static_cast<uint32_t>(FBN * rs * 4);
 
-  // prologue: the query fragments, K tile 0 (and the key biases of tile 0), then V tile 0
-  // and K tile 1
-  bf16x8 qf[D / 16];
-  load_qfrag<D>(qf, rq, row0, rs, lane);
+  // prologue: K tiles 0 and 1, V tile 0 (and its key biases)
   td.dma(k0, rk, 0, wave);
+  td.dma(v0, rv, 0, wave);
   if constexpr (KB) {
     if (wave == 0) lds_dma4(rb, kb0, kb_lane);
   }
-  td.dma(v0, rv, 0, wave);
   if (n > 1) td.dma(k1, rk, tile_bytes, wave);
+  bf16x8 qf[D / 16];
+  load_qfrag<D>(qf, rq, row0, rs, lane);
   FlashState<D> st;
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) st.o[mt] = f32x16{};
   st.m = -INFINITY;
   st.l = 0.f;
-  // loads complete in order: with at most V0's and K1's copies outstanding, the query
-  // fragments and this wave's share of K tile 0 (and the biases) have landed, so the first
-  // scores run while V0 and K1 are still in flight (row layout stage 2 -1%, bitwise unchanged)
-  constexpr int IPW = TileDma<D, NW>::IPW;
-  if (n > 1) wait_vm<2 * IPW>();
-  else wait_vm<IPW>();
+  wait_dma();
   __syncthreads();
 
   // EM: the maximum of each tile's scores is taken during the previous tile's
@@ -349,7 +343,6 @@ __device__ __forceinline__ void flash_tile(const GroupedArgs& a, int hd, int p, 
   f32x16 sa[2], sb[2];
   if (active) scores64<D>(sa, k0, fo, qf);
   if (EM && active) update_max<D>(sa, st.o, st.m, st.l, cs);
-  wait_dma();
   // iteration 0 refills K slot 0 (tile 0): every wave must be done with it
   __syncthreads();
 
