@@ -60,3 +60,18 @@ def test_chunk_and_backward_refuse_wrong_types():
         p.backward(x, x, x, x, f)
     with pytest.raises(ValueError):
         p.backward(x, x, x, x, x, grads=(x.clone(), x.clone(), f))
+
+
+def test_the_in_tree_library_runs_the_forward():
+    # the kernels that ran are the in-tree build's: it is mapped into this process, and no
+    # other copy of the library is
+    import os
+    from structured_attention_video_amd import _lib
+    p = MonarchPlan(1, 2, 128, GRID)
+    x = _t(torch.bfloat16)
+    p.forward(x, x, x)
+    torch.cuda.synchronize()
+    want = os.path.realpath(_lib.LIB_PATH)
+    maps = [line.split()[-1] for line in open("/proc/self/maps") if "libmonarch_attn" in line]
+    assert maps and all(os.path.realpath(m) == want for m in maps), maps
+    assert os.path.dirname(want) == os.path.dirname(os.path.realpath(_lib.__file__))
